@@ -1,0 +1,39 @@
+"""The seeded input generators: deterministic, per-tensor seeds, shapes."""
+import torch
+
+from expert_routing_grouped_gate_amd import workloads as W
+
+
+def test_deterministic_and_independent():
+    c = W.CONFIGS["tiny"]
+    assert torch.equal(W.draw_x(c), W.draw_x(c))
+    a13, a2 = W.draw_expert_bf16(c, 3)
+    b13, b2 = W.draw_expert_bf16(c, 3)
+    assert torch.equal(a13, b13) and torch.equal(a2, b2)
+    o13, _ = W.draw_expert_bf16(c, 4)
+    assert not torch.equal(a13, o13)
+    assert a13.shape == (2 * c.I, c.H) and a2.shape == (c.H, c.I)
+    assert a13.dtype == torch.bfloat16
+
+
+def test_distributions():
+    c = W.CONFIGS["tiny"].with_(T=256)
+    x = W.draw_x(c).float()
+    assert abs(x.std().item() - 1.0) < 0.02
+    w13, _ = W.draw_expert_bf16(c, 0)
+    assert abs(w13.float().std().item() - 0.02) < 0.001
+    assert W.draw_bias(c) is None
+    hy = W.CONFIGS["hy3"].with_(T=4, H=64, I=32, shared_I=32)
+    b = W.draw_bias(hy)
+    assert b.shape == (hy.E,) and abs(b.std().item() - 0.1) < 0.03
+    z = W.draw_bias(W.CONFIGS["qwen3_decode_w4a8"])
+    assert torch.all(z[1:] < z[:-1])     # Zipf: expert 0 most popular
+
+
+def test_mx_weights_shapes_and_codes():
+    c = W.CONFIGS["qwen3_decode_w4a8"].with_(H=256, I=128)
+    c13, s13, c2, s2 = W.draw_expert_mx(c, 0)
+    assert c13.shape == (256, 128) and s13.shape == (256, 8)
+    assert c2.shape == (256, 64) and s2.shape == (256, 4)
+    assert set(torch.unique(s13).tolist()) <= {119, 120, 121}
+    assert c13.dtype == torch.uint8
