@@ -1,0 +1,302 @@
+// C ABI of libmoe: host-side argument checks, then stream-ordered kernel
+// launches.  Declarations, argument meaning, layouts and error behaviour are
+// documented in include/moe.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+namespace {
+
+using moe::GroupedGemm;
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int check_ptrs(std::initializer_list<const void*> required) {
+  for (const void* p : required)
+    if (p == nullptr) return MOE_ERR_NULL;
+  for (const void* p : required)
+    if (!al16(p)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+int check_optional(std::initializer_list<const void*> optional) {
+  for (const void* p : optional)
+    if (p != nullptr && !al16(p)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+int check_dims_HE(int H, int E) {
+  if (H <= 0 || E <= 0) return MOE_ERR_SHAPE;
+  if (H % 256 != 0 || E > 256) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_k(int E, int k) {
+  if (k <= 0) return MOE_ERR_SHAPE;
+  if (k > E || k > 32) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_rows(int T, int k) {
+  if (T < 0) return MOE_ERR_SHAPE;
+  if ((long long)T * k >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_weights(const MoeFfnWeights* w) {
+  if (w == nullptr) return MOE_ERR_NULL;
+  int st = check_dims_HE(w->H, w->E);
+  if (st) return st;
+  if (w->I <= 0 || w->shared_I < 0) return MOE_ERR_SHAPE;
+  if (w->I % 128 != 0 || (w->shared_I % 128) != 0) return MOE_ERR_UNSUPPORTED;
+  if (w->fmt == MOE_FMT_BF16) {
+    if ((st = check_ptrs({w->w13, w->w2}))) return st;
+    if (w->shared_I > 0 && (st = check_ptrs({w->shared_w13, w->shared_w2}))) return st;
+    return MOE_OK;
+  }
+  if (w->fmt == MOE_FMT_W4A8) return MOE_ERR_UNSUPPORTED;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+// Few rows per expert -> the weight-streaming (skinny) tiles.
+inline bool small_m(long long rows, int groups) { return rows <= 16ll * groups; }
+
+GroupedGemm routed_gemm(const MoeFfnWeights* w, int T, int k, const int32_t* sorted_pair,
+                        const int32_t* offsets) {
+  GroupedGemm g{};
+  g.sorted_pair = sorted_pair;
+  g.topk = k;
+  g.offsets = offsets;
+  g.G = w->E;
+  g.ident_rows = 0;
+  g.total_rows = T * k;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is negative or inconsistent";
+    case MOE_ERR_UNSUPPORTED: return "outside the supported limits, or unknown mode/format";
+    case MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case MOE_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int moe_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
+                      void* stream) {
+  int st;
+  if ((st = check_dims_HE(H, E))) return st;
+  if (T < 0) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, wr, logits}))) return st;
+  return moe::launch_router_logits(x, wr, T, H, E, logits, as_stream(stream));
+}
+
+int moe_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,
+                  float routed_scale, float eps, int32_t* topk_ids, float* topk_w,
+                  void* stream) {
+  int st;
+  if (E <= 0) return MOE_ERR_SHAPE;
+  if (E > 256) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_k(E, k))) return st;
+  if ((st = check_rows(T, k))) return st;
+  if (mode != MOE_GATE_SOFTMAX && mode != MOE_GATE_SIGMOID) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if ((st = check_ptrs({logits, topk_ids, topk_w}))) return st;
+  if ((st = check_optional({bias}))) return st;
+  return moe::launch_gate_topk(logits, bias, T, E, k, mode, routed_scale, eps, topk_ids, topk_w,
+                               as_stream(stream));
+}
+
+size_t moe_route_workspace_size(int T, int k, int E) {
+  if (T <= 0 || k <= 0 || E <= 0) return 0;
+  return moe::route_workspace_bytes(T, k, E);
+}
+
+int moe_route(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+              int32_t* sorted_pair, int32_t* pair_pos, int32_t* dev_status, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  int st;
+  if (E <= 0) return MOE_ERR_SHAPE;
+  if (E > 256) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_k(E, k))) return st;
+  if ((st = check_rows(T, k))) return st;
+  if ((st = check_ptrs({counts, offsets}))) return st;
+  if ((st = check_optional({dev_status}))) return st;
+  if (T > 0 && (st = check_ptrs({topk_ids, sorted_pair, pair_pos}))) return st;
+  const size_t need = moe::route_workspace_bytes(T, k, E);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!al16(workspace)) return MOE_ERR_ALIGN;
+  }
+  if (T == 0) return MOE_OK;
+  return moe::launch_route(topk_ids, T, k, E, counts, offsets, sorted_pair, pair_pos, dev_status,
+                           static_cast<int32_t*>(workspace), as_stream(stream));
+}
+
+int moe_mx_quantize(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
+                    void* stream) {
+  (void)x, (void)rows, (void)cols, (void)codes, (void)scales, (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+int moe_grouped_ffn_up(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales, int T,
+                       int k, const int32_t* sorted_pair, const int32_t* offsets, void* act,
+                       uint8_t* act_scales, void* stream) {
+  int st;
+  if ((st = check_weights(w))) return st;
+  if ((st = check_k(w->E, k))) return st;
+  if ((st = check_rows(T, k))) return st;
+  if (T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, sorted_pair, offsets, act}))) return st;
+  (void)x_scales, (void)act_scales;
+  GroupedGemm g = routed_gemm(w, T, k, sorted_pair, offsets);
+  g.A = x;
+  g.gather = 1;
+  g.W = w->w13;
+  g.w_gstride = 2ll * w->I * w->H;
+  g.N = w->I;
+  g.K = w->H;
+  g.up_off = w->I;
+  g.out = act;
+  return moe::launch_ffn_up_bf16(g, small_m((long long)T * k, w->E), as_stream(stream));
+}
+
+int moe_grouped_ffn_down(const MoeFfnWeights* w, const void* act, const uint8_t* act_scales,
+                         int T, int k, const int32_t* offsets, uint16_t* y, void* stream) {
+  int st;
+  if ((st = check_weights(w))) return st;
+  if ((st = check_k(w->E, k))) return st;
+  if ((st = check_rows(T, k))) return st;
+  if (T == 0) return MOE_OK;
+  if ((st = check_ptrs({act, offsets, y}))) return st;
+  (void)act_scales;
+  GroupedGemm g = routed_gemm(w, T, k, nullptr, offsets);
+  g.A = act;
+  g.gather = 0;
+  g.W = w->w2;
+  g.w_gstride = (long long)w->H * w->I;
+  g.N = w->H;
+  g.K = w->I;
+  g.up_off = 0;
+  g.out = y;
+  return moe::launch_ffn_down_bf16(g, small_m((long long)T * k, w->E), as_stream(stream));
+}
+
+int moe_shared_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales, int T,
+                   void* shared_act, uint8_t* shared_act_scales, uint16_t* shared_y,
+                   void* stream) {
+  int st;
+  if ((st = check_weights(w))) return st;
+  if (w->shared_I <= 0) return MOE_ERR_SHAPE;
+  if (T < 0) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, shared_act, shared_y}))) return st;
+  (void)x_scales, (void)shared_act_scales;
+  GroupedGemm g{};
+  g.offsets = nullptr;
+  g.G = 1;
+  g.ident_rows = T;
+  g.total_rows = T;
+  g.gather = 0;
+  g.A = x;
+  g.W = w->shared_w13;
+  g.w_gstride = 0;
+  g.N = w->shared_I;
+  g.K = w->H;
+  g.up_off = w->shared_I;
+  g.out = shared_act;
+  const bool sm = T <= 16;
+  if ((st = moe::launch_ffn_up_bf16(g, sm, as_stream(stream)))) return st;
+  GroupedGemm d = g;
+  d.A = shared_act;
+  d.W = w->shared_w2;
+  d.N = w->H;
+  d.K = w->shared_I;
+  d.up_off = 0;
+  d.out = shared_y;
+  return moe::launch_ffn_down_bf16(d, sm, as_stream(stream));
+}
+
+int moe_grouped_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales, int T, int k,
+                    const int32_t* sorted_pair, const int32_t* offsets, void* act,
+                    uint8_t* act_scales, uint16_t* y, void* shared_act,
+                    uint8_t* shared_act_scales, uint16_t* shared_y, void* stream) {
+  int st = moe_grouped_ffn_up(w, x, x_scales, T, k, sorted_pair, offsets, act, act_scales, stream);
+  if (st) return st;
+  st = moe_grouped_ffn_down(w, act, act_scales, T, k, offsets, y, stream);
+  if (st) return st;
+  if (w->shared_I > 0 && shared_y != nullptr)
+    st = moe_shared_ffn(w, x, x_scales, T, shared_act, shared_act_scales, shared_y, stream);
+  return st;
+}
+
+int moe_combine(const uint16_t* y, const int32_t* pair_pos, const float* topk_w,
+                const uint16_t* shared_y, int T, int k, int H, uint16_t* out, void* stream) {
+  int st;
+  if (H <= 0) return MOE_ERR_SHAPE;
+  if (H % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (k <= 0) return MOE_ERR_SHAPE;
+  if (k > 32) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_rows(T, k))) return st;
+  if (T == 0) return MOE_OK;
+  if ((st = check_ptrs({y, pair_pos, topk_w, out}))) return st;
+  if ((st = check_optional({shared_y}))) return st;
+  return moe::launch_combine(y, pair_pos, topk_w, shared_y, T, k, H, out, as_stream(stream));
+}
+
+size_t moe_layer_workspace_size(const MoeLayerDesc* d, int T) {
+  if (d == nullptr || T <= 0) return 0;
+  return moe_route_workspace_size(T, d->k, d->E);
+}
+
+int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t* out,
+                      const MoeLayerBuffers* b, void* stream) {
+  int st;
+  if (d == nullptr || b == nullptr) return MOE_ERR_NULL;
+  if ((st = check_weights(&d->ffn))) return st;
+  if (d->ffn.H != d->H || d->ffn.E != d->E) return MOE_ERR_SHAPE;
+  if ((st = check_k(d->E, d->k))) return st;
+  if ((st = check_rows(T, d->k))) return st;
+  if (d->gate_mode != MOE_GATE_SOFTMAX && d->gate_mode != MOE_GATE_SIGMOID)
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, out, d->wr, b->logits, b->topk_ids, b->topk_w, b->counts, b->offsets,
+                        b->sorted_pair, b->pair_pos, b->act, b->y}))) return st;
+  if ((st = check_optional({d->bias, b->dev_status}))) return st;
+  const bool shared = d->ffn.shared_I > 0;
+  if (shared && (st = check_ptrs({b->shared_act, b->shared_y}))) return st;
+  const size_t need = moe_layer_workspace_size(d, T);
+  if (need > 0) {
+    if (b->workspace == nullptr || b->workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!al16(b->workspace)) return MOE_ERR_ALIGN;
+  }
+  const int k = d->k;
+  if ((st = moe_router_logits(x, d->wr, T, d->H, d->E, b->logits, stream))) return st;
+  if ((st = moe_gate_topk(b->logits, d->bias, T, d->E, k, d->gate_mode, d->routed_scale, d->eps,
+                          b->topk_ids, b->topk_w, stream)))
+    return st;
+  if ((st = moe_route(b->topk_ids, T, k, d->E, b->counts, b->offsets, b->sorted_pair, b->pair_pos,
+                      b->dev_status, b->workspace, b->workspace_bytes, stream)))
+    return st;
+  if ((st = moe_grouped_ffn(&d->ffn, x, nullptr, T, k, b->sorted_pair, b->offsets, b->act,
+                            nullptr, b->y, b->shared_act, nullptr, shared ? b->shared_y : nullptr,
+                            stream)))
+    return st;
+  return moe_combine(b->y, b->pair_pos, b->topk_w, shared ? b->shared_y : nullptr, T, k, d->H,
+                     out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// Shared device helpers for the gfx950 MoE kernels: bf16 conversion, wave
+// reductions, the XCD-aware block order and the device-side ragged tile
+// scheduler used by every grouped GEMM.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN -> canonical quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Streaming 16-byte load for data read exactly once (expert weights).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
+// Lane l supplies A row (l % 16), B column (l % 16), and the 8 consecutive
+// k values 8*(l/16) .. 8*(l/16)+7 of each.  D: lane l holds column (l % 16),
+// rows 4*(l/16) + {0,1,2,3}.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Hardware dispatches block b to XCD (b mod 8).  Give every XCD a contiguous
+// range of logical tile ids so that neighbouring tiles (which share weight
+// tiles) run on the same XCD and meet in its L2.  Bijective for any count.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  const int xcd = bid & 7, local = bid >> 3;
+  const int base = nblocks >> 3, rem = nblocks & 7;
+  return xcd * base + (xcd < rem ? xcd : rem) + local;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Ragged tile scheduler.  Group g owns rows [offsets[g], offsets[g+1]) and
+// ceil(rows / BM) consecutive m-slots.  For m-slot `slot`, returns the owning
+// group, its first row and the number of valid rows in the tile (<= BM), or
+// false if the slot is past the last tile.  When offsets == nullptr there is
+// a single group of `ident_rows` rows starting at row 0.  Every lane of the
+// calling wave gets the same answer; no LDS and no barrier are used.
+__device__ __forceinline__ bool find_mtile(const int* __restrict__ offsets, int G, int ident_rows,
+                                           int BM, int slot, int& g_out, int& row0, int& nrows) {
+  if (offsets == nullptr) {
+    const int r0 = slot * BM;
+    if (r0 >= ident_rows) return false;
+    g_out = 0;
+    row0 = r0;
+    nrows = min(BM, ident_rows - r0);
+    return true;
+  }
+  const int lane = threadIdx.x & 63;
+  const int per = (G + 63) >> 6;  // groups per lane (<= 5 for G <= 320)
+  const int gbeg = lane * per;
+  int tiles[5];
+  int sum = 0;
+  int prev = gbeg < G ? offsets[gbeg] : 0;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    int t = 0;
+    const int g = gbeg + i;
+    if (i < per && g < G) {
+      const int nxt = offsets[g + 1];
+      t = (nxt - prev + BM - 1) / BM;
+      prev = nxt;
+    }
+    tiles[i] = t;
+    sum += t;
+  }
+  const int incl = wave_incl_scan(sum);
+  const int excl = incl - sum;
+  const bool mine = (slot >= excl) && (slot < incl);
+  const unsigned long long bal = __ballot(mine);
+  if (bal == 0ull) return false;
+  const int src = __ffsll((long long)bal) - 1;
+  int g = 0, r0 = 0, nr = 0;
+  if (lane == src) {
+    int s = excl;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      if (i < per && slot < s + tiles[i] && slot >= s) {
+        g = gbeg + i;
+        const int lo = offsets[g];
+        const int hi = offsets[g + 1];
+        r0 = lo + (slot - s) * BM;
+        nr = min(BM, hi - r0);
+      }
+      s += tiles[i];
+    }
+  }
+  g_out = __shfl(g, src, 64);
+  row0 = __shfl(r0, src, 64);
+  nrows = __shfl(nr, src, 64);
+  return true;
+}
+
+}  // namespace moe

@@ -1,0 +1,58 @@
+// Host-side launchers of the kernels (one per step); the C ABI in api.hip
+// validates arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// MOE_ERR_LAUNCH (-5) if the runtime reports a launch error, else 0.
+inline int launch_status() { return hipGetLastError() == hipSuccess ? 0 : -5; }
+
+int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
+                         hipStream_t s);
+int launch_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,
+                     float routed_scale, float eps, int32_t* ids, float* w, hipStream_t s);
+
+size_t route_workspace_bytes(int T, int k, int E);
+int launch_route(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                 int32_t* sorted_pair, int32_t* pair_pos, int32_t* dev_status, int32_t* ws,
+                 hipStream_t s);
+
+// One grouped GEMM problem.  Rows of group g are [offsets[g], offsets[g+1])
+// (or a single identity group of ident_rows rows when offsets == nullptr).
+struct GroupedGemm {
+  const void* A;              // activations (bf16 or MXFP8 codes)
+  const uint8_t* A_scales;    // MXFP8 scales [rows, K/32] (W4A8 only)
+  const int32_t* sorted_pair; // gather: A row of sorted row r = A[sorted_pair[r] / topk]
+  int topk;
+  int gather;                 // 1: gather A rows through sorted_pair; 0: A row = r
+  const int32_t* offsets;
+  int G;
+  int ident_rows;
+  int total_rows;             // upper bound of rows over all groups (T*k or T)
+  const void* W;              // per-group weights, [N_w, K] each (bf16 or fp4 codes)
+  const uint8_t* W_scales;    // per-group E8M0 scales [N_w, K/32] (W4A8 only)
+  long long w_gstride;        // elements (bf16) or bytes (fp4 codes) between groups
+  long long ws_gstride;       // scale bytes between groups
+  int N;                      // output columns
+  int K;                      // reduction length
+  int up_off;                 // SwiGLU: row offset of the up half in W (= N)
+  void* out;                  // [rows, N] bf16, or MXFP8 codes (W4A8 GEMM1)
+  uint8_t* out_scales;        // [rows, N/32] (W4A8 GEMM1)
+};
+
+int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s);
+int launch_ffn_down_bf16(const GroupedGemm& g, bool small_m, hipStream_t s);
+int launch_ffn_up_w4a8(const GroupedGemm& g, hipStream_t s);
+int launch_ffn_down_w4a8(const GroupedGemm& g, hipStream_t s);
+
+int launch_mx_quantize(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
+                       hipStream_t s);
+
+int launch_combine(const uint16_t* y, const int32_t* pair_pos, const float* w,
+                   const uint16_t* shared_y, int T, int k, int H, uint16_t* out, hipStream_t s);
+
+}  // namespace moe

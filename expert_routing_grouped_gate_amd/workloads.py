@@ -188,3 +188,34 @@ def describe(cfg: LayerConfig) -> dict:
     d = dataclasses.asdict(cfg)
     d["R"] = cfg.R
     return d
+
+
+def draw_layer(cfg: LayerConfig, progress=None) -> dict:
+    """All inputs of one layer as CPU tensors (weights stacked over experts).
+
+    bf16: w13 [E, 2I, H], w2 [E, H, I] (+ shared_w13, shared_w2).
+    w4a8: w13 codes [E, 2I, H/2], w13_scales [E, 2I, H/32], w2 codes
+    [E, H, I/2], w2_scales [E, H, I/32]."""
+    t = {"x": draw_x(cfg), "wr": draw_router(cfg), "bias": draw_bias(cfg)}
+    E = cfg.E
+    if cfg.fmt == "bf16":
+        w13 = torch.empty((E, 2 * cfg.I, cfg.H), dtype=torch.bfloat16)
+        w2 = torch.empty((E, cfg.H, cfg.I), dtype=torch.bfloat16)
+        for e in range(E):
+            w13[e], w2[e] = draw_expert_bf16(cfg, e)
+            if progress is not None and (e % 32 == 31 or e == E - 1):
+                progress(f"{cfg.name}: drew experts 0..{e}")
+        t["w13"], t["w2"] = w13, w2
+        if cfg.shared_I:
+            t["shared_w13"], t["shared_w2"] = draw_shared_bf16(cfg)
+    else:
+        c13 = torch.empty((E, 2 * cfg.I, cfg.H // 2), dtype=torch.uint8)
+        s13 = torch.empty((E, 2 * cfg.I, cfg.H // 32), dtype=torch.uint8)
+        c2 = torch.empty((E, cfg.H, cfg.I // 2), dtype=torch.uint8)
+        s2 = torch.empty((E, cfg.H, cfg.I // 32), dtype=torch.uint8)
+        for e in range(E):
+            c13[e], s13[e], c2[e], s2[e] = draw_expert_mx(cfg, e)
+            if progress is not None and (e % 32 == 31 or e == E - 1):
+                progress(f"{cfg.name}: drew experts 0..{e}")
+        t["w13"], t["w13_scales"], t["w2"], t["w2_scales"] = c13, s13, c2, s2
+    return t

@@ -1,0 +1,110 @@
+"""Shared helpers of the GPU tests: device copies of a drawn layer and the
+oracle's view of the same inputs (fp64 numpy from the CPU tensors)."""
+import functools
+import sys
+
+import numpy as np
+import torch
+
+from expert_routing_grouped_gate_amd import binding as B
+from expert_routing_grouped_gate_amd import workloads as W
+from oracle import moe, mx
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Layer:
+    def __init__(self, cfg: W.LayerConfig, cpu: dict, dev: dict):
+        self.cfg, self.cpu, self.dev = cfg, cpu, dev
+        d = dev
+        fmt = B.FMT_W4A8 if cfg.fmt == "w4a8" else B.FMT_BF16
+        self.weights = B.ExpertWeights(
+            H=cfg.H, I=cfg.I, E=cfg.E, fmt=fmt, w13=d["w13"], w2=d["w2"],
+            w13_scales=d.get("w13_scales"), w2_scales=d.get("w2_scales"),
+            shared_I=cfg.shared_I, shared_w13=d.get("shared_w13"), shared_w2=d.get("shared_w2"))
+        self.mode = B.GATE_SIGMOID if cfg.gate == "sigmoid" else B.GATE_SOFTMAX
+
+    def layer(self):
+        return B.MoeLayer(self.weights, self.dev["wr"], self.cfg.k, self.mode, self.dev["bias"],
+                          self.cfg.routed_scale, self.cfg.eps)
+
+    # oracle views -------------------------------------------------------
+    def x64(self):
+        return self.cpu["x"].to(torch.float64).numpy()
+
+    def wr(self):
+        return self.cpu["wr"].numpy()
+
+    def bias(self):
+        b = self.cpu["bias"]
+        return None if b is None else b.numpy()
+
+    @functools.lru_cache(maxsize=8)
+    def expert(self, e):
+        c = self.cpu
+        if self.cfg.fmt == "w4a8":
+            return (mx.mxfp4_dequant(c["w13"][e].numpy(), c["w13_scales"][e].numpy(), self.cfg.H),
+                    mx.mxfp4_dequant(c["w2"][e].numpy(), c["w2_scales"][e].numpy(), self.cfg.I))
+        return (c["w13"][e].to(torch.float64).numpy(), c["w2"][e].to(torch.float64).numpy())
+
+    def shared(self):
+        c = self.cpu
+        if not self.cfg.shared_I:
+            return None
+        return (c["shared_w13"].to(torch.float64).numpy(), c["shared_w2"].to(torch.float64).numpy())
+
+    def oracle(self, logits=None, tokens=None):
+        cfg = self.cfg
+        return moe.layer_forward(self.x64(), self.wr(), cfg.k, cfg.gate, self.expert, cfg.E,
+                                 bias=self.bias(), routed_scale=cfg.routed_scale, eps=cfg.eps,
+                                 shared_weights=self.shared(), fmt=cfg.fmt, logits=logits,
+                                 tokens=tokens)
+
+
+_CACHE = {}
+_WCACHE = {}
+_WKEYS = ("w13", "w2", "w13_scales", "w2_scales", "shared_w13", "shared_w2")
+
+
+def _to_dev(d):
+    return {k: (v.to("cuda") if v is not None else None) for k, v in d.items()}
+
+
+def get_layer(cfg: W.LayerConfig) -> Layer:
+    """Inputs of cfg on the CPU and the device.  Configs of one model family
+    with equal shapes share one copy of the expert weights."""
+    if cfg not in _CACHE:
+        wkey = (cfg.family_seed, cfg.E, cfg.H, cfg.I, cfg.fmt, cfg.shared_I)
+        if wkey in _WCACHE:
+            wcpu, wdev = _WCACHE[wkey]
+            cpu = {"x": W.draw_x(cfg), "wr": W.draw_router(cfg), "bias": W.draw_bias(cfg), **wcpu}
+            dev = {**_to_dev({k: cpu[k] for k in ("x", "wr", "bias")}), **wdev}
+        else:
+            log(f"[fixture] drawing {cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} I={cfg.I}")
+            cpu = W.draw_layer(cfg, progress=log)
+            dev = _to_dev(cpu)
+            _WCACHE[wkey] = ({k: cpu[k] for k in _WKEYS if k in cpu},
+                             {k: dev[k] for k in _WKEYS if k in dev})
+        _CACHE[cfg] = Layer(cfg, cpu, dev)
+    return _CACHE[cfg]
+
+
+def drop_layers():
+    _CACHE.clear()
+    _WCACHE.clear()
+    torch.cuda.empty_cache()
+
+
+def assert_close_bf16(gpu, ref, atol, rtol, what):
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    err = np.abs(g - r)
+    bound = atol + rtol * np.abs(r)
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside |d| <= {atol} + {rtol}|ref|; "
+                             f"first at {idx.tolist()}: gpu {g[tuple(idx[0])]} ref {r[tuple(idx[0])]}; "
+                             f"max err {err.max()}")

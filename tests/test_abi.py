@@ -1,0 +1,124 @@
+"""The C-ABI library: it loads, exports every function include/moe.h
+declares, and its host-side argument checks return the documented status
+codes.  No call here reaches a kernel launch, so no GPU is needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from expert_routing_grouped_gate_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, LAUNCH, WS = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(moe_[a-z0-9_]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe.so is not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("moe_gate_topk", "moe_route", "moe_grouped_ffn", "moe_combine",
+                 "moe_layer_forward", "moe_router_logits", "moe_mx_quantize",
+                 "moe_status_string", "moe_layer_workspace_size"):
+        assert want in names
+    assert set(names) == set(B.SIGNATURES), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(B.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, LAUNCH, WS):
+        assert B.status_string(code)
+    assert B.status_string(12345) == "unknown status"
+
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address that is never dereferenced
+MIS = FAKE + 4          # misaligned
+
+
+def test_router_logits_checks(lib):
+    f = lib.moe_router_logits
+    assert f(None, FAKE, 4, 256, 8, FAKE, None) == NULL
+    assert f(FAKE, FAKE, 4, 255, 8, FAKE, None) == UNSUP        # H % 256
+    assert f(FAKE, FAKE, 4, 256, 257, FAKE, None) == UNSUP      # E > 256
+    assert f(FAKE, FAKE, -1, 256, 8, FAKE, None) == SHAPE
+    assert f(MIS, FAKE, 4, 256, 8, FAKE, None) == ALIGN
+    assert f(None, None, 0, 256, 8, None, None) == OK           # T == 0: nothing to do
+
+
+def test_gate_topk_checks(lib):
+    f = lib.moe_gate_topk
+    assert f(FAKE, None, 4, 8, 9, 0, 1.0, 1e-20, FAKE, FAKE, None) == UNSUP    # k > E
+    assert f(FAKE, None, 4, 64, 33, 0, 1.0, 1e-20, FAKE, FAKE, None) == UNSUP  # k > 32
+    assert f(FAKE, None, 4, 8, 0, 0, 1.0, 1e-20, FAKE, FAKE, None) == SHAPE
+    assert f(FAKE, None, 4, 8, 2, 7, 1.0, 1e-20, FAKE, FAKE, None) == UNSUP    # mode
+    assert f(None, None, 4, 8, 2, 0, 1.0, 1e-20, FAKE, FAKE, None) == NULL
+    assert f(FAKE, MIS, 4, 8, 2, 1, 1.0, 1e-20, FAKE, FAKE, None) == ALIGN     # bias
+    assert f(None, None, 0, 8, 2, 0, 1.0, 1e-20, None, None, None) == OK
+
+
+def test_route_checks_and_workspace(lib):
+    assert lib.moe_route_workspace_size(16, 8, 128) == 0           # one chunk
+    assert lib.moe_route_workspace_size(4096, 8, 192) == 16 * 193 * 4
+    f = lib.moe_route
+    assert f(FAKE, 4096, 8, 192, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == WS
+    assert f(FAKE, 4096, 8, 192, FAKE, FAKE, FAKE, FAKE, None, FAKE, 100, None) == WS
+    assert f(FAKE, 16, 8, 128, FAKE, None, FAKE, FAKE, None, None, 0, None) == NULL
+    assert f(FAKE, 16, 8, 128, FAKE, FAKE, FAKE, FAKE, MIS, None, 0, None) == ALIGN
+    assert f(FAKE, 16, 0, 128, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == SHAPE
+    assert f(FAKE, 1 << 28, 8, 128, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == UNSUP
+
+
+def test_ffn_checks(lib):
+    w = B.MoeFfnWeights(256, 128, 8, B.FMT_BF16, FAKE, None, FAKE, None, 0, None, None, None, None)
+    up = lib.moe_grouped_ffn_up
+    assert up(None, FAKE, None, 4, 2, FAKE, FAKE, FAKE, None, None) == NULL
+    bad = B.MoeFfnWeights(256, 100, 8, B.FMT_BF16, FAKE, None, FAKE, None, 0, None, None, None, None)
+    assert up(ctypes.byref(bad), FAKE, None, 4, 2, FAKE, FAKE, FAKE, None, None) == UNSUP  # I % 128
+    nul = B.MoeFfnWeights(256, 128, 8, B.FMT_BF16, None, None, FAKE, None, 0, None, None, None, None)
+    assert up(ctypes.byref(nul), FAKE, None, 4, 2, FAKE, FAKE, FAKE, None, None) == NULL
+    assert up(ctypes.byref(w), FAKE, None, 4, 9, FAKE, FAKE, FAKE, None, None) == UNSUP    # k > E
+    assert up(ctypes.byref(w), None, None, 4, 2, FAKE, FAKE, FAKE, None, None) == NULL
+    assert up(ctypes.byref(w), None, None, 0, 2, None, None, None, None, None) == OK
+    dn = lib.moe_grouped_ffn_down
+    assert dn(ctypes.byref(w), FAKE, None, 4, 2, None, FAKE, None) == NULL
+    sh = lib.moe_shared_ffn
+    assert sh(ctypes.byref(w), FAKE, None, 4, FAKE, None, FAKE, None) == SHAPE            # no shared expert
+
+
+def test_combine_checks(lib):
+    f = lib.moe_combine
+    assert f(FAKE, FAKE, FAKE, None, 4, 2, 100, FAKE, None) == UNSUP
+    assert f(FAKE, None, FAKE, None, 4, 2, 256, FAKE, None) == NULL
+    assert f(FAKE, FAKE, FAKE, MIS, 4, 2, 256, FAKE, None) == ALIGN
+    assert f(FAKE, FAKE, FAKE, None, 4, 33, 256, FAKE, None) == UNSUP
+
+
+def test_layer_forward_checks(lib):
+    w = B.MoeFfnWeights(256, 128, 8, B.FMT_BF16, FAKE, None, FAKE, None, 0, None, None, None, None)
+    d = B.MoeLayerDesc(256, 8, 2, 0, 1.0, 1e-20, FAKE, None, w)
+    b = B.MoeLayerBuffers()
+    f = lib.moe_layer_forward
+    assert f(None, FAKE, 4, FAKE, ctypes.byref(b), None) == NULL
+    assert f(ctypes.byref(d), FAKE, 4, FAKE, ctypes.byref(b), None) == NULL   # buffers unset
+    d2 = B.MoeLayerDesc(512, 8, 2, 0, 1.0, 1e-20, FAKE, None, w)
+    assert f(ctypes.byref(d2), FAKE, 4, FAKE, ctypes.byref(b), None) == SHAPE  # H mismatch
+    assert lib.moe_layer_workspace_size(ctypes.byref(d), 16) == 0

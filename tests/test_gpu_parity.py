@@ -1,0 +1,256 @@
+"""GPU parity: every step of the HIP path against the CPU oracle on the same
+seeded inputs, through the C ABI.  Integer outputs (ids, counts, offsets,
+permutations) must match bit for bit; floating outputs within the stated
+tolerances (bf16 layer: |d| <= 1e-2 + 1e-2*|ref|)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from expert_routing_grouped_gate_amd import binding as B
+from expert_routing_grouped_gate_amd import workloads as W
+from oracle import moe, mx
+from tests.layer_fixtures import assert_close_bf16, get_layer, log
+
+pytestmark = pytest.mark.gpu
+
+ATOL = RTOL = 1e-2
+CFG = W.CONFIGS
+
+# small layers that still span several tiles and ragged tails
+SMALL = {
+    "tiny": CFG["tiny"],
+    "tiny_T1": CFG["tiny"].with_(name="tiny_T1", T=1, x_seed=11),
+    "small_prefill": CFG["tiny"].with_(name="small_prefill", T=700, E=8, k=2, x_seed=12),
+    "small_hy3": CFG["hy3"].with_(name="small_hy3", T=301, H=256, I=128, shared_I=128, x_seed=13),
+    "small_hy3_decode": CFG["hy3"].with_(name="small_hy3_decode", T=9, H=256, I=128, shared_I=128, x_seed=14),
+    "wide_k": CFG["tiny"].with_(name="wide_k", T=40, E=256, k=32, I=128, x_seed=15, family_seed=1099),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    B.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def bf16_np(t):
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+# ------------------------------------------------------------- S1 logits ---
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_T1", "small_prefill", "small_hy3", "wide_k"])
+def test_router_logits_small(name):
+    L = get_layer(SMALL[name])
+    gl = B.router_logits(L.dev["x"], L.dev["wr"])
+    ref = moe.router_logits(L.x64(), L.wr())
+    np.testing.assert_allclose(to_np(gl), ref, atol=1e-4, rtol=0)
+
+
+# ----------------------------------------------------------- S2 gate top-k -
+
+def _gate_check(logits_gpu, k, mode, bias, scale, eps):
+    ids, w = B.gate_topk(logits_gpu, k, mode, bias, scale, eps)
+    Lc = to_np(logits_gpu)
+    bc = None if bias is None else to_np(bias)
+    rids, rw = moe.gate(Lc, k, "sigmoid" if mode == B.GATE_SIGMOID else "softmax", bc, scale, eps)
+    gi = to_np(ids)
+    assert np.array_equal(gi, rids), f"ids differ at {np.argwhere(gi != rids)[:5].tolist()}"
+    np.testing.assert_allclose(to_np(w), rw, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("mode", [B.GATE_SOFTMAX, B.GATE_SIGMOID])
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (16, 128, 8), (333, 192, 8), (64, 256, 32), (7, 8, 8), (5, 1, 1)])
+def test_gate_topk_random_and_ties(mode, T, E, k):
+    g = torch.Generator().manual_seed(T * 1000 + E + k)
+    L = torch.randn((T, E), generator=g)
+    if E >= 4:
+        L[:, E - 1] = L[:, 1]                 # exact ties between columns 1 and E-1
+        L[0, :] = 0.5                          # a fully tied row
+    bias = (torch.randn(E, generator=g) * 0.1) if mode == B.GATE_SIGMOID else None
+    scale = 2.826 if mode == B.GATE_SIGMOID else 1.0
+    _gate_check(L.cuda(), k, mode, None if bias is None else bias.cuda(), scale, 1e-20)
+
+
+def test_gate_topk_softmax_with_bias():
+    g = torch.Generator().manual_seed(7)
+    L = torch.randn((50, 128), generator=g)
+    b = W.draw_bias(CFG["qwen3_decode_w4a8"])
+    _gate_check(L.cuda(), 8, B.GATE_SOFTMAX, b.cuda(), 1.0, 1e-20)
+
+
+# -------------------------------------------------------------- S3 route ---
+
+def _distinct_ids(T, E, k, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).to(torch.int32)
+
+
+@pytest.mark.parametrize("T,E,k", [(16, 128, 8), (300, 128, 8), (4096, 192, 8), (1, 1, 1),
+                                   (5000, 256, 1), (2049, 3, 1), (256, 8, 8), (513, 256, 32)])
+def test_route_bit_exact(T, E, k):
+    ids = _distinct_ids(T, E, k, T + E + k)
+    st = torch.full((4,), 77, dtype=torch.int32, device="cuda")
+    counts, offsets, sp, pp = B.route(ids.cuda(), E, dev_status=st)
+    rc, ro, rsp, rpp = moe.route(ids.numpy(), E)
+    assert np.array_equal(to_np(counts), rc)
+    assert np.array_equal(to_np(offsets), ro)
+    assert np.array_equal(to_np(sp), rsp)
+    assert np.array_equal(to_np(pp), rpp)
+    assert int(st[0]) == 0
+
+
+def test_route_skewed_all_to_one_expert():
+    T, E, k = 3000, 64, 1
+    ids = torch.zeros((T, k), dtype=torch.int32)
+    counts, offsets, sp, pp = B.route(ids.cuda(), E)
+    rc, ro, rsp, rpp = moe.route(ids.numpy(), E)
+    assert np.array_equal(to_np(sp), rsp) and np.array_equal(to_np(offsets), ro)
+
+
+def test_route_bad_ids_flagged_and_dropped():
+    T, E, k = 2100, 16, 2
+    ids = _distinct_ids(T, E, k, 5)
+    ids[7, 1] = E          # out of range
+    ids[2000, 0] = -3
+    st = torch.zeros(4, dtype=torch.int32, device="cuda")
+    counts, offsets, sp, pp = B.route(ids.cuda(), E, dev_status=st)
+    assert int(st[0]) == B.DEV_BAD_EXPERT_ID
+    flat = ids.numpy().reshape(-1)
+    ok = (flat >= 0) & (flat < E)
+    good = np.nonzero(ok)[0]
+    order = good[np.argsort(flat[good], kind="stable")]
+    nvalid = int(to_np(offsets)[E])
+    assert nvalid == ok.sum()
+    assert np.array_equal(to_np(sp)[:nvalid], order)
+    gpp = to_np(pp)
+    assert np.all(gpp[~ok] == -1)
+    assert np.array_equal(gpp[order], np.arange(nvalid))
+    assert np.array_equal(to_np(counts), np.bincount(flat[ok], minlength=E))
+
+
+# ------------------------------------------------- S5/S6 grouped FFN paths --
+
+def _ffn_check(name):
+    L = get_layer(SMALL[name])
+    cfg = L.cfg
+    x = L.dev["x"]
+    logits = B.router_logits(x, L.dev["wr"])
+    ids, w = B.gate_topk(logits, cfg.k, L.mode, L.dev["bias"], cfg.routed_scale, cfg.eps)
+    counts, offsets, sp, pp = B.route(ids, cfg.E)
+    act, _ = B.grouped_ffn_up(L.weights, x, None, cfg.k, sp, offsets)
+    y = B.grouped_ffn_down(L.weights, act, None, cfg.T, cfg.k, offsets)
+    torch.cuda.synchronize()
+    sp_np, off_np = to_np(sp), to_np(offsets)
+    x64 = L.x64()
+    act_g, y_g = bf16_np(act), bf16_np(y)
+    for e in range(cfg.E):
+        r0, r1 = off_np[e], off_np[e + 1]
+        if r1 == r0:
+            continue
+        w13, w2 = L.expert(e)
+        xr = x64[sp_np[r0:r1] // cfg.k]
+        I = w13.shape[0] // 2
+        a = mx.bf16_round(moe.silu(xr @ w13[:I].T) * (xr @ w13[I:].T))
+        assert_close_bf16(act_g[r0:r1], a, ATOL, RTOL, f"{name} act expert {e}")
+        # GEMM2 on the GPU's own bf16 activations isolates the down projection
+        assert_close_bf16(y_g[r0:r1], act_g[r0:r1] @ w2.T, ATOL, RTOL, f"{name} y expert {e}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_T1", "small_prefill", "small_hy3", "wide_k"])
+def test_grouped_ffn_rows(name):
+    _ffn_check(name)
+
+
+@pytest.mark.parametrize("name", ["small_hy3", "small_hy3_decode"])
+def test_shared_ffn(name):
+    L = get_layer(SMALL[name])
+    _, _, sy = B.shared_ffn(L.weights, L.dev["x"])
+    ref = moe.expert_ffn(L.x64(), *L.shared())
+    assert_close_bf16(bf16_np(sy), ref, ATOL, RTOL, f"{name} shared y")
+
+
+# --------------------------------------------------------- S7 + the layer --
+
+def _layer_check(cfg, tokens=None):
+    L = get_layer(cfg)
+    layer = L.layer()
+    out = layer.forward(L.dev["x"])
+    torch.cuda.synchronize()
+    b = layer.buf
+    gl = to_np(b["logits"])
+    log(f"[{cfg.name}] layer done on GPU; oracle on {'all' if tokens is None else len(tokens)} tokens")
+    res = L.oracle(logits=gl, tokens=tokens)
+    np.testing.assert_allclose(gl, res["logits"], atol=1e-4, rtol=0)
+    assert np.array_equal(to_np(b["topk_ids"]), res["ids"])
+    np.testing.assert_allclose(to_np(b["topk_w"]), res["w"], rtol=1e-6, atol=1e-7)
+    for key in ("counts", "offsets", "sorted_pair", "pair_pos"):
+        assert np.array_equal(to_np(b[key]), res[key]), key
+    assert int(b["dev_status"][0]) == 0
+    og = bf16_np(out)
+    if tokens is not None:
+        og = og[np.asarray(tokens)]
+    assert_close_bf16(og, res["out"], ATOL, RTOL, f"{cfg.name} out")
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_T1", "small_prefill", "small_hy3", "small_hy3_decode", "wide_k"])
+def test_layer_small(name):
+    _layer_check(SMALL[name])
+
+
+def test_layer_zero_tokens():
+    L = get_layer(SMALL["tiny"])
+    layer = L.layer()
+    out = layer.forward(L.dev["x"][:0])
+    assert out.shape == (0, L.cfg.H)
+
+
+def test_layer_deterministic():
+    L = get_layer(SMALL["small_hy3"])
+    layer = L.layer()
+    a = layer.forward(L.dev["x"]).clone()
+    b = layer.forward(L.dev["x"]).clone()
+    assert torch.equal(a, b)
+
+
+def test_layer_graph_capture_replays():
+    L = get_layer(SMALL["small_prefill"])
+    layer = L.layer()
+    x = L.dev["x"]
+    out = torch.empty((x.shape[0], L.cfg.H), dtype=torch.bfloat16, device="cuda")
+    eager = layer.forward(x).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(x, out)          # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward(x, out)
+    for i in range(3):
+        out.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        layer.forward(x)               # eager work between replays
+        torch.cuda.synchronize()
+
+
+# full-size layers: GPU computes everything; routing is checked on all
+# tokens, values on a sample of tokens the oracle evaluates one by one
+FULL = [("qwen3_decode", None), ("qwen3_prefill", [0, 1, 2, 777, 2048, 4094, 4095]),
+        ("hy3", [0, 5, 1023, 1024, 3000, 4095])]
+
+
+@pytest.mark.parametrize("name,tokens", FULL, ids=[f[0] for f in FULL])
+def test_layer_full_size(name, tokens):
+    _layer_check(CFG[name], tokens)
