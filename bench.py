@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""MoE-layer forward throughput on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config qwen3_decode]
+
+One step = one moe_layer_forward call (router logits, gate top-k, routing,
+grouped GEMM1 + SwiGLU, grouped GEMM2, shared expert if any, combine) over
+one batch of synthetic tokens already resident in HBM.  W untimed warm-up
+steps, then exactly K timed steps bracketed by torch.cuda.synchronize().
+The grouped GEMM1 kernel (the largest weight stream) is timed with HIP events
+recorded by the library around its launch in every timed step; its roofline
+fraction is reported against MI355X's 8 TB/s HBM.  The CPU oracle is timed on
+a bounded sample of the same workload on the host's cores.  Prints one JSON
+line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; achieved HBM GB/s (decode) / MFMA TFLOP/s (prefill) vs peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="qwen3_decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0,
+                    help="wall-clock budget of the oracle sample")
+    return ap.parse_args()
+
+
+def workload_bytes_flops(cfg, counts):
+    """Algorithmic work of one layer call: weights of the experts the routing
+    touched (+ shared expert), router weight and bias, x in, out out; flops
+    of the routed and shared expert GEMMs."""
+    n_touched = int((counts > 0).sum())
+    R = cfg.T * cfg.k
+    if cfg.fmt == "w4a8":
+        w13_e = 2 * cfg.I * cfg.H // 2 + 2 * cfg.I * cfg.H // 32
+        w2_e = cfg.H * cfg.I // 2 + cfg.H * cfg.I // 32
+    else:
+        w13_e = 2 * cfg.I * cfg.H * 2
+        w2_e = cfg.H * cfg.I * 2
+    shared = 0
+    if cfg.shared_I:
+        shared = 3 * cfg.shared_I * cfg.H * 2
+    layer_bytes = (n_touched * (w13_e + w2_e) + shared + cfg.E * cfg.H * 4
+                   + (cfg.E * 4 if cfg.bias != "none" else 0) + 2 * cfg.T * cfg.H * 2)
+    flops = 2 * R * 3 * cfg.I * cfg.H + 2 * cfg.T * 3 * cfg.shared_I * cfg.H
+    # GEMM1 (w13 + SwiGLU) alone: touched w13 slices, x read, act written
+    act_b = R * cfg.I * (1 + 1 / 32 if cfg.fmt == "w4a8" else 2)
+    g1_bytes = n_touched * w13_e + cfg.T * cfg.H * 2 + act_b
+    g1_flops = 2 * R * 2 * cfg.I * cfg.H
+    return dict(n_touched=n_touched, layer_bytes=layer_bytes, flops=flops,
+                g1_bytes=int(g1_bytes), g1_flops=g1_flops)
+
+
+def cpu_baseline(cfg, cpu, budget_s):
+    """The oracle as it stands, token by token on the host, until the budget
+    is spent or every token is done."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+
+    from oracle import moe, mx
+
+    x = cpu["x"].to(torch.float64).numpy()
+    wr = cpu["wr"].numpy()
+    bias = None if cpu["bias"] is None else cpu["bias"].numpy()
+
+    def expert(e):
+        if cfg.fmt == "w4a8":
+            return (mx.mxfp4_dequant(cpu["w13"][e].numpy(), cpu["w13_scales"][e].numpy(), cfg.H),
+                    mx.mxfp4_dequant(cpu["w2"][e].numpy(), cpu["w2_scales"][e].numpy(), cfg.I))
+        return cpu["w13"][e].to(torch.float64).numpy(), cpu["w2"][e].to(torch.float64).numpy()
+
+    shared = None
+    if cfg.shared_I:
+        shared = (cpu["shared_w13"].to(torch.float64).numpy(), cpu["shared_w2"].to(torch.float64).numpy())
+    done = 0
+    t0 = time.perf_counter()
+    while done < cfg.T and time.perf_counter() - t0 < budget_s:
+        moe.layer_forward(x, wr, cfg.k, cfg.gate, expert, cfg.E, bias=bias, routed_scale=cfg.routed_scale,
+                          eps=cfg.eps, shared_weights=shared, fmt=cfg.fmt, tokens=[done])
+        done += 1
+    dt = time.perf_counter() - t0
+    blas = [i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    cores = max([torch.get_num_threads()] + blas)
+    return {"value": done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {done} of {cfg.T} tokens of the same layer, one oracle call per token "
+                      f"(fp64 numpy; routing over all tokens each call), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from expert_routing_grouped_gate_amd import binding as B
+    from expert_routing_grouped_gate_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.load()
+    cfg = W.CONFIGS[args.config]
+    log(f"[bench] drawing {cfg.name}")
+    cpu = W.draw_layer(cfg, progress=log)
+    dev = {k: (v.to("cuda") if v is not None else None) for k, v in cpu.items()}
+    fmt = B.FMT_W4A8 if cfg.fmt == "w4a8" else B.FMT_BF16
+    w = B.ExpertWeights(H=cfg.H, I=cfg.I, E=cfg.E, fmt=fmt, w13=dev["w13"], w2=dev["w2"],
+                        w13_scales=dev.get("w13_scales"), w2_scales=dev.get("w2_scales"),
+                        shared_I=cfg.shared_I, shared_w13=dev.get("shared_w13"),
+                        shared_w2=dev.get("shared_w2"))
+    mode = B.GATE_SIGMOID if cfg.gate == "sigmoid" else B.GATE_SOFTMAX
+    layer = B.MoeLayer(w, dev["wr"], cfg.k, mode, dev["bias"], cfg.routed_scale, cfg.eps)
+    x = dev["x"]
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    layer.alloc(cfg.T, x.device)
+
+    K, Wm = args.steps, args.warmup
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:      # materialise the event handles
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+
+    log(f"[bench] warm-up {Wm} steps")
+    for _ in range(Wm):
+        layer.forward(x, out)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {K} steps")
+    t0 = time.perf_counter()
+    for i in range(K):
+        layer.time_ffn_up(*ev[i])
+        layer.forward(x, out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    layer.time_ffn_up(None, None)
+    g1_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    ms = elapsed * 1e3 / K
+
+    counts = layer.buf["counts"].cpu().numpy()
+    wl = workload_bytes_flops(cfg, counts)
+    decode = cfg.T * cfg.k <= 16 * cfg.E
+    g1_gbs = wl["g1_bytes"] / (g1_ms * 1e-3) / 1e9
+    layer_gbs = wl["layer_bytes"] / (ms * 1e-3) / 1e9
+    layer_tflops = wl["flops"] / (ms * 1e-3) / 1e12
+    if decode or cfg.fmt == "w4a8":
+        roof = {"bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        g1_tf = wl["g1_flops"] / (g1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(g1_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(g1_tf / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof.update({"kernel": "grouped GEMM1 (w13 + SwiGLU)", "kernel_ms": round(g1_ms, 4),
+                 "algorithmic_bytes": wl["g1_bytes"], "algorithmic_flops": wl["g1_flops"]})
+
+    cpu_b = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        cpu_b = cpu_baseline(cfg, cpu, args.cpu_budget_s)
+
+    desc = (f"{cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} top-{cfg.k} {cfg.gate}"
+            f"{' x%.3f' % cfg.routed_scale if cfg.gate == 'sigmoid' else ''} I={cfg.I}"
+            f"{' shared I=%d' % cfg.shared_I if cfg.shared_I else ''} {cfg.fmt}")
+    res = {
+        "metric": METRIC, "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4xmxfp8" if cfg.fmt == "w4a8" else "bf16", "data": "synthetic",
+        "config": {"workload": desc, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                   "experts_touched": wl["n_touched"], "parallelism": "single GPU"},
+        "layer": {"hbm_gbs": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
+                  "tflops": round(layer_tflops, 2), "mfma_frac": round(layer_tflops / BF16_PEAK_TFLOPS, 4),
+                  "algorithmic_bytes": wl["layer_bytes"], "flops": wl["flops"]},
+        "roofline": roof,
+        "cpu_baseline": cpu_b,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

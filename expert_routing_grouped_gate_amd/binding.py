@@ -51,7 +51,8 @@ class MoeLayerBuffers(_c.Structure):
                 ("offsets", _vp), ("sorted_pair", _vp), ("pair_pos", _vp), ("dev_status", _vp),
                 ("xq", _vp), ("xq_scales", _vp), ("act", _vp), ("act_scales", _vp), ("y", _vp),
                 ("shared_act", _vp), ("shared_act_scales", _vp), ("shared_y", _vp),
-                ("workspace", _vp), ("workspace_bytes", _c.c_size_t)]
+                ("workspace", _vp), ("workspace_bytes", _c.c_size_t),
+                ("ev_ffn_up_begin", _vp), ("ev_ffn_up_end", _vp)]
 
 
 # name -> (restype, argtypes); mirrors include/moe.h
@@ -298,9 +299,18 @@ class MoeLayer:
         b["workspace"] = torch.empty(max(nws, 16), dtype=torch.uint8, device=device)
         self.buf = b
         self.cbuf = MoeLayerBuffers(**{n: _ptr(b.get(n)) for n, _ in MoeLayerBuffers._fields_
-                                       if n != "workspace_bytes"}, workspace_bytes=nws)
+                                       if n not in ("workspace_bytes", "ev_ffn_up_begin", "ev_ffn_up_end")},
+                                    workspace_bytes=nws)
         self._T = T
         return b
+
+    def time_ffn_up(self, begin: Optional[torch.cuda.Event], end: Optional[torch.cuda.Event]):
+        """Have later forward calls record these events (created by torch,
+        already recorded once so that their handles exist) around the
+        grouped GEMM1 launch; None, None to stop."""
+        assert self._T is not None, "call alloc() or forward() first"
+        self.cbuf.ev_ffn_up_begin = None if begin is None else begin.cuda_event
+        self.cbuf.ev_ffn_up_end = None if end is None else end.cuda_event
 
     def forward(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
         _dev(x)

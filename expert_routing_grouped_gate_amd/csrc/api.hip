@@ -291,9 +291,18 @@ int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t*
   if ((st = moe_route(b->topk_ids, T, k, d->E, b->counts, b->offsets, b->sorted_pair, b->pair_pos,
                       b->dev_status, b->workspace, b->workspace_bytes, stream)))
     return st;
-  if ((st = moe_grouped_ffn(&d->ffn, x, nullptr, T, k, b->sorted_pair, b->offsets, b->act,
-                            nullptr, b->y, b->shared_act, nullptr, shared ? b->shared_y : nullptr,
-                            stream)))
+  hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(b->ev_ffn_up_begin);
+  hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(b->ev_ffn_up_end);
+  const bool timed = ev0 != nullptr && ev1 != nullptr;
+  if (timed && hipEventRecord(ev0, as_stream(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
+  if ((st = moe_grouped_ffn_up(&d->ffn, x, nullptr, T, k, b->sorted_pair, b->offsets, b->act,
+                               nullptr, stream)))
+    return st;
+  if (timed && hipEventRecord(ev1, as_stream(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
+  if ((st = moe_grouped_ffn_down(&d->ffn, b->act, nullptr, T, k, b->offsets, b->y, stream)))
+    return st;
+  if (shared && (st = moe_shared_ffn(&d->ffn, x, nullptr, T, b->shared_act, nullptr, b->shared_y,
+                                     stream)))
     return st;
   return moe_combine(b->y, b->pair_pos, b->topk_w, shared ? b->shared_y : nullptr, T, k, d->H,
                      out, stream);

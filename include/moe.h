@@ -244,6 +244,11 @@ typedef struct {
   uint16_t* shared_y;     /* [T, H] */
   void* workspace;        /* moe_layer_workspace_size(desc, T) bytes */
   size_t workspace_bytes;
+  /* Optional hipEvent_t handles, recorded on `stream` right before and right
+   * after the grouped GEMM1 (w13 + SwiGLU) launch so that a caller can time
+   * that kernel inside a full layer call; NULL to skip. */
+  void* ev_ffn_up_begin;
+  void* ev_ffn_up_end;
 } MoeLayerBuffers;
 
 size_t moe_layer_workspace_size(const MoeLayerDesc* d, int T);
