@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "launch.hpp"
 
 namespace {
@@ -58,7 +58,13 @@ int check_weights(const MoeFfnWeights* w) {
     if (w->shared_I > 0 && (st = check_ptrs({w->shared_w13, w->shared_w2}))) return st;
     return MOE_OK;
   }
-  if (w->fmt == MOE_FMT_W4A8) return MOE_ERR_UNSUPPORTED;
+  if (w->fmt == MOE_FMT_W4A8) {
+    if ((st = check_ptrs({w->w13, w->w13_scales, w->w2, w->w2_scales}))) return st;
+    if (w->shared_I > 0 &&
+        (st = check_ptrs({w->shared_w13, w->shared_w13_scales, w->shared_w2, w->shared_w2_scales})))
+      return st;
+    return MOE_OK;
+  }
   return MOE_ERR_UNSUPPORTED;
 }
 
@@ -148,8 +154,12 @@ int moe_route(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int
 
 int moe_mx_quantize(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
                     void* stream) {
-  (void)x, (void)rows, (void)cols, (void)codes, (void)scales, (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  int st;
+  if (rows < 0 || cols <= 0) return MOE_ERR_SHAPE;
+  if (cols % 32 != 0 || (long long)rows * cols >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if ((st = check_ptrs({x, codes, scales}))) return st;
+  return moe::launch_mx_quantize(x, rows, cols, codes, scales, as_stream(stream));
 }
 
 int moe_grouped_ffn_up(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales, int T,
@@ -161,16 +171,25 @@ int moe_grouped_ffn_up(const MoeFfnWeights* w, const void* x, const uint8_t* x_s
   if ((st = check_rows(T, k))) return st;
   if (T == 0) return MOE_OK;
   if ((st = check_ptrs({x, sorted_pair, offsets, act}))) return st;
-  (void)x_scales, (void)act_scales;
+  const bool mx = w->fmt == MOE_FMT_W4A8;
+  if (mx && (st = check_ptrs({x_scales, act_scales}))) return st;
   GroupedGemm g = routed_gemm(w, T, k, sorted_pair, offsets);
   g.A = x;
+  g.A_scales = x_scales;
   g.gather = 1;
   g.W = w->w13;
-  g.w_gstride = 2ll * w->I * w->H;
+  g.W_scales = w->w13_scales;
   g.N = w->I;
   g.K = w->H;
   g.up_off = w->I;
   g.out = act;
+  g.out_scales = act_scales;
+  if (mx) {
+    g.w_gstride = (long long)w->I * w->H;  // bytes: 2I rows of H/2
+    g.ws_gstride = 2ll * w->I * (w->H / 32);
+    return moe::launch_ffn_up_w4a8(g, as_stream(stream));
+  }
+  g.w_gstride = 2ll * w->I * w->H;
   return moe::launch_ffn_up_bf16(g, small_m((long long)T * k, w->E), as_stream(stream));
 }
 
@@ -182,16 +201,24 @@ int moe_grouped_ffn_down(const MoeFfnWeights* w, const void* act, const uint8_t*
   if ((st = check_rows(T, k))) return st;
   if (T == 0) return MOE_OK;
   if ((st = check_ptrs({act, offsets, y}))) return st;
-  (void)act_scales;
+  const bool mx = w->fmt == MOE_FMT_W4A8;
+  if (mx && (st = check_ptrs({act_scales}))) return st;
   GroupedGemm g = routed_gemm(w, T, k, nullptr, offsets);
   g.A = act;
+  g.A_scales = act_scales;
   g.gather = 0;
   g.W = w->w2;
-  g.w_gstride = (long long)w->H * w->I;
+  g.W_scales = w->w2_scales;
   g.N = w->H;
   g.K = w->I;
   g.up_off = 0;
   g.out = y;
+  if (mx) {
+    g.w_gstride = (long long)w->H * (w->I / 2);
+    g.ws_gstride = (long long)w->H * (w->I / 32);
+    return moe::launch_ffn_down_w4a8(g, as_stream(stream));
+  }
+  g.w_gstride = (long long)w->H * w->I;
   return moe::launch_ffn_down_bf16(g, small_m((long long)T * k, w->E), as_stream(stream));
 }
 
@@ -204,7 +231,8 @@ int moe_shared_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scale
   if (T < 0) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if ((st = check_ptrs({x, shared_act, shared_y}))) return st;
-  (void)x_scales, (void)shared_act_scales;
+  const bool mx = w->fmt == MOE_FMT_W4A8;
+  if (mx && (st = check_ptrs({x_scales, shared_act_scales}))) return st;
   GroupedGemm g{};
   g.offsets = nullptr;
   g.G = 1;
@@ -212,22 +240,30 @@ int moe_shared_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scale
   g.total_rows = T;
   g.gather = 0;
   g.A = x;
+  g.A_scales = x_scales;
   g.W = w->shared_w13;
+  g.W_scales = w->shared_w13_scales;
   g.w_gstride = 0;
+  g.ws_gstride = 0;
   g.N = w->shared_I;
   g.K = w->H;
   g.up_off = w->shared_I;
   g.out = shared_act;
+  g.out_scales = shared_act_scales;
   const bool sm = T <= 16;
-  if ((st = moe::launch_ffn_up_bf16(g, sm, as_stream(stream)))) return st;
+  st = mx ? moe::launch_ffn_up_w4a8(g, as_stream(stream)) : moe::launch_ffn_up_bf16(g, sm, as_stream(stream));
+  if (st) return st;
   GroupedGemm d = g;
   d.A = shared_act;
+  d.A_scales = shared_act_scales;
   d.W = w->shared_w2;
+  d.W_scales = w->shared_w2_scales;
   d.N = w->H;
   d.K = w->shared_I;
   d.up_off = 0;
   d.out = shared_y;
-  return moe::launch_ffn_down_bf16(d, sm, as_stream(stream));
+  d.out_scales = nullptr;
+  return mx ? moe::launch_ffn_down_w4a8(d, as_stream(stream)) : moe::launch_ffn_down_bf16(d, sm, as_stream(stream));
 }
 
 int moe_grouped_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales, int T, int k,
@@ -277,13 +313,19 @@ int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t*
                         b->sorted_pair, b->pair_pos, b->act, b->y}))) return st;
   if ((st = check_optional({d->bias, b->dev_status}))) return st;
   const bool shared = d->ffn.shared_I > 0;
+  const bool mx = d->ffn.fmt == MOE_FMT_W4A8;
   if (shared && (st = check_ptrs({b->shared_act, b->shared_y}))) return st;
+  if (mx && (st = check_ptrs({b->xq, b->xq_scales, b->act_scales}))) return st;
+  if (mx && shared && (st = check_ptrs({b->shared_act_scales}))) return st;
   const size_t need = moe_layer_workspace_size(d, T);
   if (need > 0) {
     if (b->workspace == nullptr || b->workspace_bytes < need) return MOE_ERR_WORKSPACE;
     if (!al16(b->workspace)) return MOE_ERR_ALIGN;
   }
   const int k = d->k;
+  if (mx && (st = moe_mx_quantize(x, T, d->H, b->xq, b->xq_scales, stream))) return st;
+  const void* xin = mx ? static_cast<const void*>(b->xq) : static_cast<const void*>(x);
+  const uint8_t* xin_s = mx ? b->xq_scales : nullptr;
   if ((st = moe_router_logits(x, d->wr, T, d->H, d->E, b->logits, stream))) return st;
   if ((st = moe_gate_topk(b->logits, d->bias, T, d->E, k, d->gate_mode, d->routed_scale, d->eps,
                           b->topk_ids, b->topk_w, stream)))
@@ -295,14 +337,14 @@ int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t*
   hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(b->ev_ffn_up_end);
   const bool timed = ev0 != nullptr && ev1 != nullptr;
   if (timed && hipEventRecord(ev0, as_stream(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
-  if ((st = moe_grouped_ffn_up(&d->ffn, x, nullptr, T, k, b->sorted_pair, b->offsets, b->act,
-                               nullptr, stream)))
+  if ((st = moe_grouped_ffn_up(&d->ffn, xin, xin_s, T, k, b->sorted_pair, b->offsets, b->act,
+                               b->act_scales, stream)))
     return st;
   if (timed && hipEventRecord(ev1, as_stream(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
-  if ((st = moe_grouped_ffn_down(&d->ffn, b->act, nullptr, T, k, b->offsets, b->y, stream)))
+  if ((st = moe_grouped_ffn_down(&d->ffn, b->act, b->act_scales, T, k, b->offsets, b->y, stream)))
     return st;
-  if (shared && (st = moe_shared_ffn(&d->ffn, x, nullptr, T, b->shared_act, nullptr, b->shared_y,
-                                     stream)))
+  if (shared && (st = moe_shared_ffn(&d->ffn, xin, xin_s, T, b->shared_act, b->shared_act_scales,
+                                     b->shared_y, stream)))
     return st;
   return moe_combine(b->y, b->pair_pos, b->topk_w, shared ? b->shared_y : nullptr, T, k, d->H,
                      out, stream);

@@ -4,10 +4,10 @@
 // compute decomposition": w13 = gate rows then up rows, SwiGLU =
 // SiLU(first half) * second half, fused here into the GEMM1 epilogue).
 //
-// Tiles are scheduled on the device from the routing offsets (find_mtile):
-// the grid covers ceil(rows/BM) + groups m-slots per n-tile, an upper bound
-// of the real tile count, and surplus blocks exit at once.  Nothing is read
-// back to the host, so the launch is graph-capturable.
+// Tiles are scheduled on the device from the routing offsets (TileMap): a
+// persistent grid of resident blocks walks the real tile list, whose length
+// every block computes from the offsets.  Nothing is read back to the host,
+// so the launch is graph-capturable.
 //
 // Two tile shapes of one scheduling scheme:
 //  * skinny (few rows per expert: decode).  A block covers 16 rows; each
@@ -27,17 +27,8 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.f + expf(-g))
 
 // ------------------------------------------------------------- skinny -----
 template <bool SWIGLU, int WN, int WK, int U>
-__global__ __launch_bounds__(64 * WN * WK) void ffn_skinny(GroupedGemm g, int m_slots) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wn = wave % WN;
-  const int wk = wave / WN;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int n_tile = id / m_slots;
-  const int slot = id - n_tile * m_slots;
-  int grp, row0, nrows;
-  if (!find_mtile(g.offsets, g.G, g.ident_rows, 16, slot, grp, row0, nrows)) return;
-
+__device__ __forceinline__ void skinny_tile(const GroupedGemm& g, int lane, int wn, int wk,
+                                            int n_tile, int grp, int row0, int nrows) {
   const int li = lane & 15;        // weight row (A operand) / activation row (B operand)
   const int kq = (lane >> 4) * 8;  // this lane's 8 k values inside a 32-step
   const int n0 = n_tile * 16 * WN + wn * 16;
@@ -82,12 +73,16 @@ __global__ __launch_bounds__(64 * WN * WK) void ffn_skinny(GroupedGemm g, int m_
       red[wk - 1][wn][1][lane] = accu;
     }
     __syncthreads();
-    if (wk != 0) return;
+    if (wk != 0) {
+      __syncthreads();  // red[] is reused by the next tile
+      return;
+    }
 #pragma unroll
     for (int w = 0; w < WK - 1; ++w) {
       accg += red[w][wn][0][lane];
       accu += red[w][wn][1][lane];
     }
+    __syncthreads();
   }
 
   // D[n][m]: this lane holds activation row li, output columns n0 + 4*(lane>>4) + i
@@ -103,24 +98,37 @@ __global__ __launch_bounds__(64 * WN * WK) void ffn_skinny(GroupedGemm g, int m_
   }
 }
 
+template <bool SWIGLU, int WN, int WK, int U>
+__global__ __launch_bounds__(64 * WN * WK) void ffn_skinny(GroupedGemm g, int n_tiles) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wn = wave % WN;
+  const int wk = wave / WN;
+  TileMap tm;
+  tm.init(g.offsets, g.G, g.ident_rows, 16);
+  const int total = tm.total * n_tiles;
+  // persistent: block b takes tiles b, b + gridDim.x, ... (gridDim.x % 8 == 0
+  // keeps every tile of a block on the block's XCD)
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    const int id = xcd_remap(t, total);
+    const int n_tile = id / tm.total;
+    int grp, row0, nrows;
+    tm.find(id - n_tile * tm.total, grp, row0, nrows);
+    skinny_tile<SWIGLU, WN, WK, U>(g, lane, wn, wk, n_tile, grp, row0, nrows);
+  }
+}
+
 // -------------------------------------------------------------- tiled -----
 constexpr int TBM = 128, TBN = 128, TBK = 64;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
 template <bool SWIGLU>
-__global__ __launch_bounds__(256, 2) void ffn_tiled(GroupedGemm g, int m_slots) {
-  // [buffer][A rows 0..127 | B rows 128..255][8 chunks of 16 B]
-  __shared__ u32x4 smem[2][(TBM + TBN) * 8];
+__device__ __forceinline__ void tiled_tile(const GroupedGemm& g, u32x4 (*smem)[(TBM + TBN) * 8],
+                                           int n_tile, int grp, int row0, int nrows) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int n_tile = id / m_slots;
-  const int slot = id - n_tile * m_slots;
-  int grp, row0, nrows;
-  if (!find_mtile(g.offsets, g.G, g.ident_rows, TBM, slot, grp, row0, nrows)) return;
-
   constexpr int BNOUT = SWIGLU ? TBN / 2 : TBN;
   const int n0 = n_tile * BNOUT;
   const int K = g.K;
@@ -238,41 +246,79 @@ __global__ __launch_bounds__(256, 2) void ffn_tiled(GroupedGemm g, int m_slots) 
       *reinterpret_cast<u32x4*>(out + (size_t)(row0 + row) * g.N + n0 + c * 8) =
           *reinterpret_cast<const u32x4*>(ct + row * CST + c * 8);
   }
+  __syncthreads();  // the next tile overwrites the LDS
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256, 2) void ffn_tiled(GroupedGemm g, int n_tiles) {
+  // [buffer][A rows 0..127 | B rows 128..255][8 chunks of 16 B]
+  __shared__ u32x4 smem[2][(TBM + TBN) * 8];
+  TileMap tm;
+  tm.init(g.offsets, g.G, g.ident_rows, TBM);
+  const int total = tm.total * n_tiles;
+  for (int t = blockIdx.x; t < total; t += gridDim.x) {
+    const int id = xcd_remap(t, total);
+    const int n_tile = id / tm.total;
+    int grp, row0, nrows;
+    tm.find(id - n_tile * tm.total, grp, row0, nrows);
+    tiled_tile<SWIGLU>(g, smem, n_tile, grp, row0, nrows);
+  }
 }
 
 // ----------------------------------------------------------- launchers ----
-static inline int m_slots_for(const GroupedGemm& g, int BM) {
+// Persistent grids: (resident blocks per CU) x (CUs), a multiple of 8, capped
+// by an upper bound of the tile count.
+template <typename Kern>
+static int persistent_grid(Kern kernel, int block, long long max_tiles) {
+  static int cache[64];  // per device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    int cus = 0, occ = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0) != hipSuccess || occ <= 0)
+      occ = 1;
+    cache[dev] = ((cus * occ + 7) / 8) * 8;
+  }
+  long long cap = ((max_tiles + 7) / 8) * 8;
+  return (int)(cap < cache[dev] ? cap : cache[dev]);
+}
+
+static inline long long tiles_bound(const GroupedGemm& g, int BM, int n_tiles) {
   const int groups = g.offsets ? g.G : 1;
-  return (g.total_rows + BM - 1) / BM + groups;
+  return ((long long)(g.total_rows + BM - 1) / BM + groups) * n_tiles;
+}
+
+template <bool SWIGLU, int WN, int WK, int U>
+static void launch_skinny(const GroupedGemm& g, hipStream_t s) {
+  const int nt = g.N / (16 * WN);
+  auto k = ffn_skinny<SWIGLU, WN, WK, U>;
+  const int grid = persistent_grid(k, 64 * WN * WK, tiles_bound(g, 16, nt));
+  hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WN * WK), 0, s, g, nt);
+}
+
+template <bool SWIGLU>
+static void launch_tiled(const GroupedGemm& g, hipStream_t s) {
+  const int nt = g.N / (SWIGLU ? TBN / 2 : TBN);
+  auto k = ffn_tiled<SWIGLU>;
+  const int grid = persistent_grid(k, 256, tiles_bound(g, TBM, nt));
+  hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, g, nt);
 }
 
 int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
-  if (small_m) {
-    constexpr int WN = 1, WK = 4, U = 8;
-    const int ms = m_slots_for(g, 16);
-    const int nt = g.N / (16 * WN);
-    hipLaunchKernelGGL((ffn_skinny<true, WN, WK, U>), dim3(nt * ms), dim3(64 * WN * WK), 0, s, g,
-                       ms);
-  } else {
-    const int ms = m_slots_for(g, TBM);
-    const int nt = g.N / (TBN / 2);
-    hipLaunchKernelGGL(ffn_tiled<true>, dim3(nt * ms), dim3(256), 0, s, g, ms);
-  }
+  if (small_m)
+    launch_skinny<true, 1, 4, 8>(g, s);
+  else
+    launch_tiled<true>(g, s);
   return launch_status();
 }
 
 int launch_ffn_down_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
-  if (small_m) {
-    constexpr int WN = 4, WK = 1, U = 8;
-    const int ms = m_slots_for(g, 16);
-    const int nt = g.N / (16 * WN);
-    hipLaunchKernelGGL((ffn_skinny<false, WN, WK, U>), dim3(nt * ms), dim3(64 * WN * WK), 0, s, g,
-                       ms);
-  } else {
-    const int ms = m_slots_for(g, TBM);
-    const int nt = g.N / TBN;
-    hipLaunchKernelGGL(ffn_tiled<false>, dim3(nt * ms), dim3(256), 0, s, g, ms);
-  }
+  if (small_m)
+    launch_skinny<false, 4, 1, 8>(g, s);
+  else
+    launch_tiled<false>(g, s);
   return launch_status();
 }
 

@@ -13,37 +13,48 @@
 namespace moe {
 
 // ---------------------------------------------------------------- S1 ------
-// Few tokens (decode): one wave per (expert, 16-token tile).  The wave
-// streams one router row once and dots it with up to 16 token rows (which
-// stay in L2); lanes split H in 4-element slices, then a butterfly reduces
-// each token's partial sums.  Fixed order -> deterministic.
+// Few tokens (decode): one block of 256 threads per (expert, 16-token tile).
+// Every thread issues all its loads for a 4096-wide slice of H at once (4
+// float4 of the router row, 4 x 8 bytes of each token row), so one memory
+// latency covers the slice; then the block reduces the 16 partial sums
+// (wave butterfly, then the 4 waves through LDS).  Fixed order ->
+// deterministic.
 __global__ __launch_bounds__(256) void router_logits_small(const uint16_t* __restrict__ x,
                                                            const float* __restrict__ wr, int T,
                                                            int H, int E,
                                                            float* __restrict__ logits) {
-  const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int ntt = (T + 15) >> 4;
-  const int e = wid / ntt;
-  const int tt = wid - e * ntt;
-  if (e >= E) return;
-  const int t0 = tt * 16;
+  __shared__ float part[4][16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x;
+  const int t0 = blockIdx.y * 16;
   const int nt = min(16, T - t0);
+  const float* wrow = wr + (size_t)e * H;
+  const uint16_t* xt = x + (size_t)t0 * H;
   float acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  const float* wrow = wr + (size_t)e * H;
-  for (int h = lane * 4; h < H; h += 256) {
-    const float4 w4 = *reinterpret_cast<const float4*>(wrow + h);
+  for (int hb = 0; hb < H; hb += 4096) {
+    float4 w4[4];
+    u32x2 xv[4][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i < nt) {
-        const u32x2 xv = *reinterpret_cast<const u32x2*>(x + (size_t)(t0 + i) * H + h);
+    for (int j = 0; j < 4; ++j) {
+      const int h = hb + j * 1024 + tid * 4;
+      const bool ok = h < H;
+      w4[j] = ok ? *reinterpret_cast<const float4*>(wrow + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        xv[j][i] = (ok && i < nt) ? *reinterpret_cast<const u32x2*>(xt + (size_t)i * H + h) : u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
         float a = acc[i];
-        a = fmaf(bf16_to_f32(xv.x & 0xffffu), w4.x, a);
-        a = fmaf(bf16_to_f32(xv.x >> 16), w4.y, a);
-        a = fmaf(bf16_to_f32(xv.y & 0xffffu), w4.z, a);
-        a = fmaf(bf16_to_f32(xv.y >> 16), w4.w, a);
+        a = fmaf(bf16_to_f32(xv[j][i].x & 0xffffu), w4[j].x, a);
+        a = fmaf(bf16_to_f32(xv[j][i].x >> 16), w4[j].y, a);
+        a = fmaf(bf16_to_f32(xv[j][i].y & 0xffffu), w4[j].z, a);
+        a = fmaf(bf16_to_f32(xv[j][i].y >> 16), w4[j].w, a);
         acc[i] = a;
       }
     }
@@ -53,15 +64,10 @@ __global__ __launch_bounds__(256) void router_logits_small(const uint16_t* __res
     float v = acc[i];
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    acc[i] = v;
+    if (lane == 0) part[wave][i] = v;
   }
-  if (lane < nt) {
-    float v = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i == lane) v = acc[i];
-    logits[(size_t)(t0 + lane) * E + e] = v;
-  }
+  __syncthreads();
+  if (tid < nt) logits[(size_t)(t0 + tid) * E + e] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
 }
 
 // Many tokens (prefill): LDS-tiled fp32 product, block tile 64 tokens x 32
@@ -129,8 +135,7 @@ __global__ __launch_bounds__(256) void router_logits_tiled(const uint16_t* __res
 int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
                          hipStream_t s) {
   if (T <= 64) {
-    const int waves = E * ((T + 15) / 16);
-    hipLaunchKernelGGL(router_logits_small, dim3((waves + 3) / 4), dim3(256), 0, s, x, wr, T, H,
+    hipLaunchKernelGGL(router_logits_small, dim3(E, (T + 15) / 16), dim3(256), 0, s, x, wr, T, H,
                        E, logits);
   } else {
     hipLaunchKernelGGL(router_logits_tiled, dim3((T + RT_TT - 1) / RT_TT, (E + RT_TE - 1) / RT_TE),

@@ -1,0 +1,119 @@
+"""GPU parity of the W4A8 path (MXFP4 weights, MXFP8 activations): the
+dynamic MX quantiser bit for bit, each scaled-MFMA GEMM against the oracle on
+the GPU's own inputs, and the whole layer within |d| <= 3e-2 + 3e-2*|ref|."""
+import numpy as np
+import pytest
+import torch
+
+from expert_routing_grouped_gate_amd import binding as B
+from expert_routing_grouped_gate_amd import workloads as W
+from oracle import moe, mx
+from tests.layer_fixtures import assert_close_bf16, get_layer
+
+pytestmark = pytest.mark.gpu
+
+ATOL = RTOL = 3e-2
+CFG = W.CONFIGS
+SMALL = {
+    "mx_tiny": CFG["qwen3_decode_w4a8"].with_(name="mx_tiny", T=16, H=256, E=8, k=2, I=128,
+                                              family_seed=1105, x_seed=21),
+    "mx_mid": CFG["qwen3_decode_w4a8"].with_(name="mx_mid", T=37, H=1024, E=16, k=4, I=256,
+                                             family_seed=1106, x_seed=22),
+    "mx_decode_shape": CFG["qwen3_decode_w4a8"].with_(name="mx_decode_shape", T=5, x_seed=23),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    B.load()
+
+
+def np_(t):
+    return t.detach().cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,cols,scale", [(16, 4096, 1.0), (3, 256, 1e-3), (1, 32, 300.0), (7, 96, 1e-30)])
+def test_mx_quantize_bit_exact(rows, cols, scale):
+    g = torch.Generator().manual_seed(rows * 7 + cols)
+    x = (torch.randn((rows, cols), generator=g) * scale)
+    x[0, :32] = 0.0                                   # an all-zero block
+    if cols >= 64:
+        x[0, 32:64] = torch.linspace(-448, 448, 32)   # saturating values
+    x = x.to(torch.bfloat16)
+    codes, scales = B.mx_quantize(x.cuda())
+    rc, rs = mx.mxfp8_quantize(x.to(torch.float64).numpy())
+    assert np.array_equal(np_(scales), rs)
+    assert np.array_equal(np_(codes), rc)
+
+
+def _quant_codes_close(gpu_codes, gpu_scales, ref_vals, what):
+    """The GPU quantises fp32 values, the oracle the fp64 ones; allow a code
+    to differ by one E4M3 step on a small fraction of elements (values that
+    sit next to a rounding boundary)."""
+    gv = mx.mxfp8_dequant(gpu_codes, gpu_scales)
+    rc, rs = mx.mxfp8_quantize(ref_vals)
+    rv = mx.mxfp8_dequant(rc, rs)
+    same = gv == rv
+    assert same.mean() > 0.995, f"{what}: only {same.mean():.4f} of codes equal"
+    d = np.abs(gv - rv)
+    assert np.all(d <= np.abs(rv) * 0.126 + np.repeat(mx.e8m0_decode(rs), 32, -1) * 2.0 ** -9 * 1.01), what
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_mx_grouped_ffn(name):
+    L = get_layer(SMALL[name])
+    cfg = L.cfg
+    x = L.dev["x"]
+    xq, xs = B.mx_quantize(x)
+    logits = B.router_logits(x, L.dev["wr"])
+    ids, w = B.gate_topk(logits, cfg.k, L.mode, L.dev["bias"], cfg.routed_scale, cfg.eps)
+    counts, offsets, sp, pp = B.route(ids, cfg.E)
+    act, act_s = B.grouped_ffn_up(L.weights, xq, xs, cfg.k, sp, offsets)
+    y = B.grouped_ffn_down(L.weights, act, act_s, cfg.T, cfg.k, offsets)
+    torch.cuda.synchronize()
+    xv = mx.mxfp8_dequant(np_(xq), np_(xs))
+    sp_np, off = np_(sp), np_(offsets)
+    act_c, act_sc = np_(act), np_(act_s)
+    act_v = mx.mxfp8_dequant(act_c, act_sc)
+    yg = np_(y.float()).astype(np.float64)
+    for e in range(cfg.E):
+        r0, r1 = off[e], off[e + 1]
+        if r1 == r0:
+            continue
+        w13, w2 = L.expert(e)
+        xr = xv[sp_np[r0:r1] // cfg.k]
+        I = w13.shape[0] // 2
+        a = moe.silu(xr @ w13[:I].T) * (xr @ w13[I:].T)
+        _quant_codes_close(act_c[r0:r1], act_sc[r0:r1], a, f"{name} act expert {e}")
+        # the down projection on the GPU's own activation codes
+        assert_close_bf16(yg[r0:r1], act_v[r0:r1] @ w2.T, 1e-2, 1e-2, f"{name} y expert {e}")
+
+
+def _layer_check(cfg, tokens=None):
+    L = get_layer(cfg)
+    layer = L.layer()
+    out = layer.forward(L.dev["x"])
+    torch.cuda.synchronize()
+    b = layer.buf
+    gl = np_(b["logits"])
+    res = L.oracle(logits=gl, tokens=tokens)
+    np.testing.assert_allclose(gl, res["logits"], atol=1e-4, rtol=0)
+    assert np.array_equal(np_(b["topk_ids"]), res["ids"])
+    for key in ("counts", "offsets", "sorted_pair", "pair_pos"):
+        assert np.array_equal(np_(b[key]), res[key]), key
+    rc, rs = mx.mxfp8_quantize(L.x64())
+    assert np.array_equal(np_(b["xq"]), rc) and np.array_equal(np_(b["xq_scales"]), rs)
+    og = out.double().cpu().numpy()
+    if tokens is not None:
+        og = og[np.asarray(tokens)]
+    assert_close_bf16(og, res["out"], ATOL, RTOL, f"{cfg.name} out")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_mx_layer_small(name):
+    _layer_check(SMALL[name])
+
+
+def test_mx_layer_full_decode():
+    _layer_check(CFG["qwen3_decode_w4a8"])
