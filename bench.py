@@ -40,7 +40,21 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (5 times) and "
+                         "exit: the reference for scaling HBM byte counters")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {mib} MiB 5 times")
 
 
 def workload_bytes_flops(cfg, counts):
@@ -118,6 +132,9 @@ def main():
     from expert_routing_grouped_gate_amd import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
     B.load()
     cfg = W.CONFIGS[args.config]
     log(f"[bench] drawing {cfg.name}")
