@@ -13,7 +13,8 @@
 //  * skinny (few rows per expert: decode).  A block covers 16 rows; each
 //    wave streams 16 weight rows (SwiGLU: 16 gate + 16 up rows) straight
 //    from HBM into MFMA operand registers (each weight byte is used once),
-//    with U K-steps of loads in flight; waves may split K and reduce in LDS.
+//    double-buffered in batches of U K-steps; waves may split K and reduce
+//    in LDS.
 //  * tiled (many rows per expert: prefill).  128 x 128 block tile, K step 64,
 //    both operands staged through double-buffered, XOR-swizzled LDS; 2 x 2
 //    waves each own a 64 x 64 sub-tile of 16x16x32 MFMAs; the epilogue goes
@@ -44,22 +45,38 @@ __device__ __forceinline__ void skinny_tile(const GroupedGemm& g, int lane, int 
 
   f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
   const int nsteps = Kw / 32;
-  int st = 0;
-  for (; st + U <= nsteps; st += U) {
-    u32x4 wa[U], wb[U], xa[U];
+  // Two register batches of U K-steps: the loads of batch b+1 are issued
+  // before the MFMAs of batch b (the scheduling barrier keeps the compiler
+  // from interleaving them), so up to 2U steps of loads are in flight.
+  u32x4 wa0[U], wb0[U], xa0[U], wa1[U], wb1[U], xa1[U];
+  auto issue = [&](u32x4* wa, u32x4* wb, u32x4* xa, int st) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       wa[u] = ld16_stream(Wp + (st + u) * 32);
       if (SWIGLU) wb[u] = ld16_stream(Wp + upoff + (st + u) * 32);
       xa[u] = ld16(Ap + (st + u) * 32);
     }
+  };
+  auto compute = [&](const u32x4* wa, const u32x4* wb, const u32x4* xa) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       accg = mfma16x16x32(wa[u], xa[u], accg);
       if (SWIGLU) accu = mfma16x16x32(wb[u], xa[u], accu);
     }
+  };
+  const int nb = nsteps / U;
+  if (nb > 0) issue(wa0, wb0, xa0, 0);
+  for (int b = 0; b < nb; b += 2) {
+    if (b + 1 < nb) issue(wa1, wb1, xa1, (b + 1) * U);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wa0, wb0, xa0);
+    if (b + 1 < nb) {
+      if (b + 2 < nb) issue(wa0, wb0, xa0, (b + 2) * U);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wa1, wb1, xa1);
+    }
   }
-  for (; st < nsteps; ++st) {
+  for (int st = nb * U; st < nsteps; ++st) {
     const u32x4 wa = ld16_stream(Wp + st * 32);
     const u32x4 xa = ld16(Ap + st * 32);
     accg = mfma16x16x32(wa, xa, accg);
@@ -308,7 +325,7 @@ static void launch_tiled(const GroupedGemm& g, hipStream_t s) {
 
 int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (small_m)
-    launch_skinny<true, 1, 4, 8>(g, s);
+    launch_skinny<true, 1, 4, 4>(g, s);
   else
     launch_tiled<true>(g, s);
   return launch_status();
@@ -316,7 +333,7 @@ int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
 
 int launch_ffn_down_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (small_m)
-    launch_skinny<false, 4, 1, 8>(g, s);
+    launch_skinny<false, 4, 1, 4>(g, s);
   else
     launch_tiled<false>(g, s);
   return launch_status();
