@@ -70,64 +70,96 @@ __global__ __launch_bounds__(256) void router_logits_small(const uint16_t* __res
   if (tid < nt) logits[(size_t)(t0 + tid) * E + e] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
 }
 
-// Many tokens (prefill): LDS-tiled fp32 product, block tile 64 tokens x 32
-// experts, K step 32; each thread owns 4 tokens x 2 experts.
-constexpr int RT_TT = 64, RT_TE = 32, RT_BK = 32;
+// Many tokens (prefill): the product on bf16 MFMA, exactly.  Each fp32
+// router weight is split into three bf16 terms, w = hi + mid + lo (hi and mid
+// are truncations, lo is the exact remainder: 8 + 8 + 8 significand bits), so
+// x * w = x*hi + x*mid + x*lo where every product of the bf16 x with a term
+// is exact in fp32; the MFMA accumulates the three products in fp32.  Block
+// tile 32 tokens x 64 experts, K step 32, operands staged in double-buffered
+// LDS (the split is done once, by the loading thread); wave w owns experts
+// 16w..16w+15 of the tile and both 16-token halves (6 MFMAs per K step).
+constexpr int RM_TT = 32, RM_TE = 64;
 
-__global__ __launch_bounds__(256) void router_logits_tiled(const uint16_t* __restrict__ x,
-                                                           const float* __restrict__ wr, int T,
-                                                           int H, int E,
-                                                           float* __restrict__ logits) {
-  __shared__ float xs[RT_BK][RT_TT + 4];
-  __shared__ float ws[RT_BK][RT_TE + 4];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * RT_TT;
-  const int e0 = blockIdx.y * RT_TE;
-  const int tx = tid & 15, ty = tid >> 4;
-  float acc[4][2] = {};
-  // load assignments
-  const int xl_tok = tid >> 2, xl_h = (tid & 3) * 8;
-  const int wl_e = tid >> 3, wl_h = (tid & 7) * 4;
-  const int xtok = min(t0 + xl_tok, T - 1);
-  const int we = min(e0 + wl_e, E - 1);
-  const uint16_t* xp = x + (size_t)xtok * H + xl_h;
-  const float* wp = wr + (size_t)we * H + wl_h;
-  for (int h0 = 0; h0 < H; h0 += RT_BK) {
-    const u32x4 xv = ld16(xp + h0);
-    const float4 wv = *reinterpret_cast<const float4*>(wp + h0);
-    __syncthreads();
+__device__ __forceinline__ void split3_bf16(const float* w8, u32x4& hi, u32x4& mid, u32x4& lo) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xs[xl_h + 2 * i][xl_tok] = bf16_to_f32(xv[i] & 0xffffu);
-      xs[xl_h + 2 * i + 1][xl_tok] = bf16_to_f32(xv[i] >> 16);
-    }
-    ws[wl_h + 0][wl_e] = wv.x;
-    ws[wl_h + 1][wl_e] = wv.y;
-    ws[wl_h + 2][wl_e] = wv.z;
-    ws[wl_h + 3][wl_e] = wv.w;
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < RT_BK; ++kk) {
-      const float4 a = *reinterpret_cast<const float4*>(&xs[kk][ty * 4]);
-      const float2 b = *reinterpret_cast<const float2*>(&ws[kk][tx * 2]);
-      acc[0][0] = fmaf(a.x, b.x, acc[0][0]);
-      acc[0][1] = fmaf(a.x, b.y, acc[0][1]);
-      acc[1][0] = fmaf(a.y, b.x, acc[1][0]);
-      acc[1][1] = fmaf(a.y, b.y, acc[1][1]);
-      acc[2][0] = fmaf(a.z, b.x, acc[2][0]);
-      acc[2][1] = fmaf(a.z, b.y, acc[2][1]);
-      acc[3][0] = fmaf(a.w, b.x, acc[3][0]);
-      acc[3][1] = fmaf(a.w, b.y, acc[3][1]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
+  for (int q = 0; q < 4; ++q) {
+    uint32_t h2 = 0, m2 = 0, l2 = 0;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int e = e0 + tx * 2 + j;
-      if (e < E) logits[(size_t)t * E + e] = acc[i][j];
+      const float w = w8[2 * q + j];
+      const uint32_t hb = __float_as_uint(w) & 0xffff0000u;   // truncation: top 8 bits
+      const float r1 = w - __uint_as_float(hb);                  // exact
+      const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+      const float r2 = r1 - __uint_as_float(mb);                 // exact, <= 8 bits
+      const uint32_t lb = f32_to_bf16(r2);                        // exact
+      h2 |= (hb >> 16) << (16 * j);
+      m2 |= (mb >> 16) << (16 * j);
+      l2 |= lb << (16 * j);
+    }
+    hi[q] = h2;
+    mid[q] = m2;
+    lo[q] = l2;
+  }
+}
+
+__global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ wr, int T,
+                                                          int H, int E,
+                                                          float* __restrict__ logits) {
+  __shared__ u32x4 xs[2][RM_TT * 4];
+  __shared__ u32x4 ws[2][3][RM_TE * 4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * RM_TT, e0 = blockIdx.y * RM_TE;
+  // loaders: threads 0..127 -> x (token tid/4, chunk tid%4); all -> wr (expert tid/4, chunk tid%4)
+  const int lrow = tid >> 2, lch = tid & 3;
+  const uint16_t* xp = x + (size_t)min(t0 + (lrow & 31), T - 1) * H + lch * 8;
+  const float* wp = wr + (size_t)min(e0 + lrow, E - 1) * H + lch * 8;
+  u32x4 rx;
+  float rw[8];
+  auto gload = [&](int k0) {
+    if (tid < 128) rx = ld16(xp + k0);
+    const float4 a = *reinterpret_cast<const float4*>(wp + k0);
+    const float4 b = *reinterpret_cast<const float4*>(wp + k0 + 4);
+    rw[0] = a.x; rw[1] = a.y; rw[2] = a.z; rw[3] = a.w;
+    rw[4] = b.x; rw[5] = b.y; rw[6] = b.z; rw[7] = b.w;
+  };
+  auto lstore = [&](int buf) {
+    if (tid < 128) xs[buf][lrow * 4 + lch] = rx;
+    u32x4 h, m, l;
+    split3_bf16(rw, h, m, l);
+    ws[buf][0][lrow * 4 + lch] = h;
+    ws[buf][1][lrow * 4 + lch] = m;
+    ws[buf][2][lrow * 4 + lch] = l;
+  };
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, fc = lane >> 4;
+  const int nk = H / 32;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * 32);
+    const u32x4 a0 = xs[buf][fr * 4 + fc];
+    const u32x4 a1 = xs[buf][(16 + fr) * 4 + fc];
+#pragma unroll
+    for (int sp = 0; sp < 3; ++sp) {
+      const u32x4 b = ws[buf][sp][(16 * wave + fr) * 4 + fc];
+      acc0 = mfma16x16x32(a0, b, acc0);
+      acc1 = mfma16x16x32(a1, b, acc1);
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  // D[m][n]: lane holds expert 16*wave + (lane & 15), tokens 4*(lane>>4) + i
+  const int e = e0 + 16 * wave + fr;
+  if (e < E) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ta = t0 + 4 * fc + i, tb = t0 + 16 + 4 * fc + i;
+      if (ta < T) logits[(size_t)ta * E + e] = acc0[i];
+      if (tb < T) logits[(size_t)tb * E + e] = acc1[i];
     }
   }
 }
@@ -138,7 +170,7 @@ int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E
     hipLaunchKernelGGL(router_logits_small, dim3(E, (T + 15) / 16), dim3(256), 0, s, x, wr, T, H,
                        E, logits);
   } else {
-    hipLaunchKernelGGL(router_logits_tiled, dim3((T + RT_TT - 1) / RT_TT, (E + RT_TE - 1) / RT_TE),
+    hipLaunchKernelGGL(router_logits_mfma, dim3((T + RM_TT - 1) / RM_TT, (E + RM_TE - 1) / RM_TE),
                        dim3(256), 0, s, x, wr, T, H, E, logits);
   }
   return launch_status();

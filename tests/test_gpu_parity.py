@@ -55,6 +55,25 @@ def test_router_logits_small(name):
     np.testing.assert_allclose(to_np(gl), ref, atol=1e-4, rtol=0)
 
 
+@pytest.mark.parametrize("T", [16, 200])
+def test_router_logits_exact_when_sums_are_exact(T):
+    """x in {-1, 0, 1} with 4 non-zeros per row and router weights with full
+    24-bit significands below 1/4: every partial sum is exact in fp32, so
+    both router kernels (FMA for few tokens, three-term bf16 MFMA for many)
+    must return the exact logits bit for bit."""
+    H, E = 256, 24
+    g = torch.Generator().manual_seed(T)
+    x = torch.zeros((T, H))
+    for t in range(T):
+        idx = torch.randperm(H, generator=g)[:4]
+        x[t, idx] = torch.randint(0, 2, (4,), generator=g).float() * 2 - 1
+    k = torch.randint(-(1 << 21), 1 << 21, (E, H), generator=g).double()
+    wr = (k * 2.0 ** -23).float()
+    exact = (x.double() @ wr.double().T)
+    got = B.router_logits(x.to(torch.bfloat16).cuda(), wr.cuda())
+    assert torch.equal(got.cpu().double(), exact)
+
+
 # ----------------------------------------------------------- S2 gate top-k -
 
 def _gate_check(logits_gpu, k, mode, bias, scale, eps):
