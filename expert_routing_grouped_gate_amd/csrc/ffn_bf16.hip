@@ -15,10 +15,12 @@
 //    from HBM into MFMA operand registers (each weight byte is used once),
 //    double-buffered in batches of U K-steps; waves may split K and reduce
 //    in LDS.
-//  * tiled (many rows per expert: prefill).  128 x 128 block tile, K step 64,
-//    both operands staged through double-buffered, XOR-swizzled LDS; 2 x 2
-//    waves each own a 64 x 64 sub-tile of 16x16x32 MFMAs; the epilogue goes
-//    through LDS so global stores are 16-byte and row-contiguous.
+//  * tiled (many rows per expert: prefill).  128 x 256 block tile (256
+//    weight rows), K step 64, both operands staged through double-buffered,
+//    XOR-swizzled LDS; 2 x 2 waves each own a 64 x 128 sub-tile of 16x16x32
+//    MFMAs (the larger wave tile halves LDS reads per MFMA against 64 x 64);
+//    the epilogue goes through LDS so global stores are 16-byte and
+//    row-contiguous.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -136,128 +138,171 @@ __global__ __launch_bounds__(64 * WN * WK) void ffn_skinny(GroupedGemm g, int n_
 }
 
 // -------------------------------------------------------------- tiled -----
-constexpr int TBM = 128, TBN = 128, TBK = 64;
+// Block tile BM x BN (BN weight rows; with SwiGLU the first BN/2 are gate
+// rows n0.., the last BN/2 the matching up rows), K step 64, WM x WN waves,
+// each owning a (BM/WM) x (BN/WN) sub-tile of 16x16x32 MFMAs.  Operands are
+// staged through two XOR-swizzled LDS buffers: the global loads of step k+1
+// are in flight while step k computes.
+constexpr int TBK = 64;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
-template <bool SWIGLU>
-__device__ __forceinline__ void tiled_tile(const GroupedGemm& g, u32x4 (*smem)[(TBM + TBN) * 8],
-                                           int n_tile, int grp, int row0, int nrows) {
+template <bool SWIGLU, int BM, int BN, int WM, int WN>
+struct Tiled {
+  static constexpr int NW = WM * WN;
+  static constexpr int NTHR = 64 * NW;
+  static constexpr int TM = BM / WM, TN = BN / WN;
+  static constexpr int MT = TM / 16, NT = TN / 16;
+  static constexpr int BNOUT = SWIGLU ? BN / 2 : BN;
+  static constexpr int STAGE = (BM + BN) * 8;  // u32x4 entries per LDS stage
+  static constexpr int NSTAGE = 3;
+  static constexpr int LPW = (BM + BN) / 8 / NW;  // 1 KB loads per wave per stage
+  static_assert((BM + BN) % (8 * NW) == 0, "row groups split evenly over waves");
+  static_assert(!SWIGLU || NT % 2 == 0, "gate/up pairs");
+  static_assert(BM * (BNOUT + 8) * 2 <= NSTAGE * STAGE * 16, "epilogue tile fits");
+};
+
+// s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt left open (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One output tile.  LDS holds NSTAGE stages of [A rows 0..BM-1 | B rows
+// BM..BM+BN-1] x 8 chunks of 16 B (one K step of 64), chunk c of row r stored
+// at c ^ (r & 7).  Stages are filled by global_load_lds_dwordx4: each wave
+// instruction writes 1 KB = 8 rows, lane l taking row l/8, physical chunk
+// l%8, so it loads logical chunk (l%8) ^ (l/8).  Step k+2 is in flight while
+// step k computes; waits are explicit (vmcnt counts this wave's DMA loads)
+// and the block barrier carries no memory fence, so the loads of the next
+// step stay in flight across it.
+template <bool SWIGLU, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void tiled_tile(const GroupedGemm& g, u32x4* smem, int n_tile, int grp,
+                                           int row0, int nrows) {
+  using C = Tiled<SWIGLU, BM, BN, WM, WN>;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  constexpr int BNOUT = SWIGLU ? TBN / 2 : TBN;
-  const int n0 = n_tile * BNOUT;
+  const int wm = wave % WM, wn = wave / WM;
+  const int n0 = n_tile * C::BNOUT;
   const int K = g.K;
   const uint16_t* Wg = static_cast<const uint16_t*>(g.W) + (size_t)grp * g.w_gstride;
 
-  // global -> LDS assignment: 4 A chunks and 4 B chunks of 16 B per thread
-  const uint16_t* aptr[4];
-  const uint16_t* bptr[4];
-  const int lchunk = tid & 7;
+  const uint16_t* src[C::LPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 3) + 32 * i;
-    const int r = row0 + min(row, nrows - 1);
-    const int arow = g.gather ? g.sorted_pair[r] / g.topk : r;
-    aptr[i] = static_cast<const uint16_t*>(g.A) + (size_t)arow * K + lchunk * 8;
-    int wrow;
-    if (SWIGLU)
-      wrow = row < 64 ? n0 + row : g.up_off + n0 + (row - 64);
-    else
-      wrow = n0 + row;
-    bptr[i] = Wg + (size_t)wrow * K + lchunk * 8;
+  for (int i = 0; i < C::LPW; ++i) {
+    const int rg = wave + C::NW * i;
+    const int row = rg * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ (lane >> 3);
+    if (row < BM) {
+      const int r = row0 + min(row, nrows - 1);
+      const int arow = g.gather ? g.sorted_pair[r] / g.topk : r;
+      src[i] = static_cast<const uint16_t*>(g.A) + (size_t)arow * K + c * 8;
+    } else {
+      const int br = row - BM;
+      int wrow;
+      if (SWIGLU)
+        wrow = br < BN / 2 ? n0 + br : g.up_off + n0 + (br - BN / 2);
+      else
+        wrow = n0 + br;
+      src[i] = Wg + (size_t)wrow * K + c * 8;
+    }
   }
-
-  f32x4 acc[4][4];
+  auto issue = [&](int buf, int k0) {
+    u32x4* st = smem + buf * C::STAGE;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ld16(aptr[i] + k0);
-      rb[i] = ld16_stream(bptr[i] + k0);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = (tid >> 3) + 32 * i;
-      smem[buf][swz(row, lchunk)] = ra[i];
-      smem[buf][swz(TBM + row, lchunk)] = rb[i];
+    for (int i = 0; i < C::LPW; ++i) {
+      const int rg = wave + C::NW * i;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src[i] + k0),
+          (__attribute__((address_space(3))) void*)(st + rg * 64), 16, 0, 0);
     }
   };
 
-  // fragment rows inside the LDS tile
-  int arow_l[4], brow_l[4];
+  f32x4 acc[C::MT][C::NT];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) arow_l[mi] = wm * 64 + mi * 16 + (lane & 15);
+  for (int a = 0; a < C::MT; ++a)
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
+    for (int b = 0; b < C::NT; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int arow_l[C::MT], brow_l[C::NT];
+#pragma unroll
+  for (int mi = 0; mi < C::MT; ++mi) arow_l[mi] = wm * C::TM + mi * 16 + (lane & 15);
+#pragma unroll
+  for (int ni = 0; ni < C::NT; ++ni) {
     int rr;
     if (SWIGLU)
-      rr = (ni < 2) ? wn * 32 + ni * 16 : 64 + wn * 32 + (ni - 2) * 16;
+      rr = (ni < C::NT / 2) ? wn * (C::TN / 2) + ni * 16
+                            : BN / 2 + wn * (C::TN / 2) + (ni - C::NT / 2) * 16;
     else
-      rr = wn * 64 + ni * 16;
-    brow_l[ni] = TBM + rr + (lane & 15);
+      rr = wn * C::TN + ni * 16;
+    brow_l[ni] = BM + rr + (lane & 15);
   }
   const int kc = lane >> 4;
 
   const int nk = K / TBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  issue(0, 0);
+  if (nk > 1) issue(1, TBK);
+  int buf = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * TBK);
+    if (kt + 1 < nk)
+      wait_vm_lgkm0<C::LPW>();
+    else
+      wait_vm_lgkm0<0>();
+    block_barrier();
+    if (kt + 2 < nk) issue(buf == 0 ? 2 : buf - 1, (kt + 2) * TBK);
+    const u32x4* st = smem + buf * C::STAGE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      u32x4 af[4], bfr[4];
+      u32x4 af[C::MT], bfr[C::NT];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) af[mi] = smem[buf][swz(arow_l[mi], ks * 4 + kc)];
+      for (int mi = 0; mi < C::MT; ++mi) af[mi] = st[swz(arow_l[mi], ks * 4 + kc)];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) bfr[ni] = smem[buf][swz(brow_l[ni], ks * 4 + kc)];
+      for (int ni = 0; ni < C::NT; ++ni) bfr[ni] = st[swz(brow_l[ni], ks * 4 + kc)];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < C::MT; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma16x16x32(af[mi], bfr[ni], acc[mi][ni]);
+        for (int ni = 0; ni < C::NT; ++ni) acc[mi][ni] = mfma16x16x32(af[mi], bfr[ni], acc[mi][ni]);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+    buf = buf == 2 ? 0 : buf + 1;
   }
+  wait_vm_lgkm0<0>();
+  block_barrier();  // every wave is done with the stages before the C tile reuses them
 
-  // epilogue through LDS: C tile [128][BNOUT] bf16, rows padded by 16 B
-  constexpr int CST = BNOUT + 8;  // elements per LDS row
-  uint16_t* ct = reinterpret_cast<uint16_t*>(&smem[0][0]);
+  // epilogue through LDS: C tile [BM][BNOUT] bf16, rows padded by 16 B
+  constexpr int CST = C::BNOUT + 8;
+  uint16_t* ct = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+  for (int mi = 0; mi < C::MT; ++mi) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
+      const int m = wm * C::TM + mi * 16 + 4 * (lane >> 4) + i;
       if (SWIGLU) {
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          const int n = wn * 32 + gi * 16 + (lane & 15);
-          const float a = silu_f32(acc[mi][gi][i]) * acc[mi][gi + 2][i];
+        for (int ni = 0; ni < C::NT / 2; ++ni) {
+          const int n = wn * (C::TN / 2) + ni * 16 + (lane & 15);
+          const float a = silu_f32(acc[mi][ni][i]) * acc[mi][ni + C::NT / 2][i];
           ct[m * CST + n] = (uint16_t)f32_to_bf16(a);
         }
       } else {
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int n = wn * 64 + ni * 16 + (lane & 15);
+        for (int ni = 0; ni < C::NT; ++ni) {
+          const int n = wn * C::TN + ni * 16 + (lane & 15);
           ct[m * CST + n] = (uint16_t)f32_to_bf16(acc[mi][ni][i]);
         }
       }
     }
   }
   __syncthreads();
-  constexpr int CPR = BNOUT / 8;  // 16-byte chunks per row
+  constexpr int CPR = C::BNOUT / 8;  // 16-byte chunks per row
   uint16_t* out = static_cast<uint16_t*>(g.out);
-  for (int idx = tid; idx < TBM * CPR; idx += 256) {
+  for (int idx = tid; idx < BM * CPR; idx += C::NTHR) {
     const int row = idx / CPR, c = idx - row * CPR;
     if (row < nrows)
       *reinterpret_cast<u32x4*>(out + (size_t)(row0 + row) * g.N + n0 + c * 8) =
@@ -266,19 +311,19 @@ __device__ __forceinline__ void tiled_tile(const GroupedGemm& g, u32x4 (*smem)[(
   __syncthreads();  // the next tile overwrites the LDS
 }
 
-template <bool SWIGLU>
-__global__ __launch_bounds__(256, 2) void ffn_tiled(GroupedGemm g, int n_tiles) {
-  // [buffer][A rows 0..127 | B rows 128..255][8 chunks of 16 B]
-  __shared__ u32x4 smem[2][(TBM + TBN) * 8];
+template <bool SWIGLU, int BM, int BN, int WM, int WN, int OCC>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void ffn_tiled(GroupedGemm g, int n_tiles) {
+  using C = Tiled<SWIGLU, BM, BN, WM, WN>;
+  __shared__ u32x4 smem[C::NSTAGE * C::STAGE];
   TileMap tm;
-  tm.init(g.offsets, g.G, g.ident_rows, TBM);
+  tm.init(g.offsets, g.G, g.ident_rows, BM);
   const int total = tm.total * n_tiles;
   for (int t = blockIdx.x; t < total; t += gridDim.x) {
     const int id = xcd_remap(t, total);
     const int n_tile = id / tm.total;
     int grp, row0, nrows;
     tm.find(id - n_tile * tm.total, grp, row0, nrows);
-    tiled_tile<SWIGLU>(g, smem, n_tile, grp, row0, nrows);
+    tiled_tile<SWIGLU, BM, BN, WM, WN>(g, smem, n_tile, grp, row0, nrows);
   }
 }
 
@@ -315,19 +360,19 @@ static void launch_skinny(const GroupedGemm& g, hipStream_t s) {
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WN * WK), 0, s, g, nt);
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, int BM, int BN, int WM, int WN, int OCC>
 static void launch_tiled(const GroupedGemm& g, hipStream_t s) {
-  const int nt = g.N / (SWIGLU ? TBN / 2 : TBN);
-  auto k = ffn_tiled<SWIGLU>;
-  const int grid = persistent_grid(k, 256, tiles_bound(g, TBM, nt));
-  hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, g, nt);
+  const int nt = g.N / (SWIGLU ? BN / 2 : BN);
+  auto k = ffn_tiled<SWIGLU, BM, BN, WM, WN, OCC>;
+  const int grid = persistent_grid(k, 64 * WM * WN, tiles_bound(g, BM, nt));
+  hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WM * WN), 0, s, g, nt);
 }
 
 int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (small_m)
     launch_skinny<true, 1, 4, 4>(g, s);
   else
-    launch_tiled<true>(g, s);
+    launch_tiled<true, 128, 256, 2, 4, 1>(g, s);
   return launch_status();
 }
 
@@ -335,7 +380,7 @@ int launch_ffn_down_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (small_m)
     launch_skinny<false, 4, 1, 4>(g, s);
   else
-    launch_tiled<false>(g, s);
+    launch_tiled<false, 128, 256, 2, 4, 1>(g, s);
   return launch_status();
 }
 
