@@ -147,7 +147,7 @@ constexpr int TBK = 64;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
-template <bool SWIGLU, int BM, int BN, int WM, int WN>
+template <bool SWIGLU, int BM, int BN, int WM, int WN, int NS>
 struct Tiled {
   static constexpr int NW = WM * WN;
   static constexpr int NTHR = 64 * NW;
@@ -155,18 +155,40 @@ struct Tiled {
   static constexpr int MT = TM / 16, NT = TN / 16;
   static constexpr int BNOUT = SWIGLU ? BN / 2 : BN;
   static constexpr int STAGE = (BM + BN) * 8;  // u32x4 entries per LDS stage
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = NS;  // LDS stages; NS - 1 K-steps in flight
   static constexpr int LPW = (BM + BN) / 8 / NW;  // 1 KB loads per wave per stage
   static_assert((BM + BN) % (8 * NW) == 0, "row groups split evenly over waves");
   static_assert(!SWIGLU || NT % 2 == 0, "gate/up pairs");
   static_assert(BM * (BNOUT + 8) * 2 <= NSTAGE * STAGE * 16, "epilogue tile fits");
 };
 
+// s_waitcnt lgkmcnt(n) only (vmcnt and expcnt left open; gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
+}
+
 // s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt left open (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// s_waitcnt vmcnt(n) only (lgkmcnt and expcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Make the compiler treat these registers as read here, so that it waits
+// for their pending LDS loads at this point (its own, tracked wait).
+template <int N>
+__device__ __forceinline__ void use_regs(const u32x4* r) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(r[i]));
 }
 
 __device__ __forceinline__ void block_barrier() {
@@ -183,10 +205,10 @@ __device__ __forceinline__ void block_barrier() {
 // step k computes; waits are explicit (vmcnt counts this wave's DMA loads)
 // and the block barrier carries no memory fence, so the loads of the next
 // step stay in flight across it.
-template <bool SWIGLU, int BM, int BN, int WM, int WN>
+template <bool SWIGLU, int BM, int BN, int WM, int WN, int NS>
 __device__ __forceinline__ void tiled_tile(const GroupedGemm& g, u32x4* smem, int n_tile, int grp,
                                            int row0, int nrows) {
-  using C = Tiled<SWIGLU, BM, BN, WM, WN>;
+  using C = Tiled<SWIGLU, BM, BN, WM, WN, NS>;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
@@ -246,31 +268,73 @@ __device__ __forceinline__ void tiled_tile(const GroupedGemm& g, u32x4* smem, in
   }
   const int kc = lane >> 4;
 
+  // Software pipeline over half-steps (K = 32): the fragments of the next
+  // half-step are read from LDS while the MFMAs of the current one run.
+  // Iteration k: read stage k's second half -> F1; MFMAs on F0 (first half);
+  // wait for this wave's DMA of stage k+1; barrier (stage k+1 is complete for
+  // every wave and stage k's buffer is free); DMA of stage k+NS into stage
+  // k's buffer; read stage k+1's first half -> F0; MFMAs on F1.
+  static_assert(NS >= 2, "at least two stages");
   const int nk = K / TBK;
-  issue(0, 0);
-  if (nk > 1) issue(1, TBK);
+#pragma unroll
+  for (int p = 0; p < NS; ++p)
+    if (p < nk) issue(p, p * TBK);
+  u32x4 af0[C::MT], bf0[C::NT], af1[C::MT], bf1[C::NT];
+  auto read_frags = [&](u32x4* af, u32x4* bfr, int b, int ks) {
+    const u32x4* st = smem + b * C::STAGE;
+#pragma unroll
+    for (int mi = 0; mi < C::MT; ++mi) af[mi] = st[swz(arow_l[mi], ks * 4 + kc)];
+#pragma unroll
+    for (int ni = 0; ni < C::NT; ++ni) bfr[ni] = st[swz(brow_l[ni], ks * 4 + kc)];
+  };
+  auto mfmas = [&](const u32x4* af, const u32x4* bfr) {
+#pragma unroll
+    for (int mi = 0; mi < C::MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < C::NT; ++ni) acc[mi][ni] = mfma16x16x32(af[mi], bfr[ni], acc[mi][ni]);
+  };
+  // stage 0 ready -> first half into F0
+  if (nk > NS - 1)
+    wait_vm_lgkm0<(NS - 1) * C::LPW>();
+  else
+    wait_vm_lgkm0<0>();
+  block_barrier();
+  read_frags(af0, bf0, 0, 0);
+  // retire every scalar load here: with none pending, the LDS reads in the
+  // loop can be waited for by count (scalar loads return out of order)
+  wait_lgkm<0>();
   int buf = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk)
-      wait_vm_lgkm0<C::LPW>();
-    else
-      wait_vm_lgkm0<0>();
-    block_barrier();
-    if (kt + 2 < nk) issue(buf == 0 ? 2 : buf - 1, (kt + 2) * TBK);
-    const u32x4* st = smem + buf * C::STAGE;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 af[C::MT], bfr[C::NT];
-#pragma unroll
-      for (int mi = 0; mi < C::MT; ++mi) af[mi] = st[swz(arow_l[mi], ks * 4 + kc)];
-#pragma unroll
-      for (int ni = 0; ni < C::NT; ++ni) bfr[ni] = st[swz(brow_l[ni], ks * 4 + kc)];
-#pragma unroll
-      for (int mi = 0; mi < C::MT; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < C::NT; ++ni) acc[mi][ni] = mfma16x16x32(af[mi], bfr[ni], acc[mi][ni]);
+    read_frags(af1, bf1, buf, 1);
+    // F0 was requested before F1 and LDS reads complete in order: waiting
+    // until at most F1's reads are pending leaves those in flight during the
+    // MFMAs below
+    wait_lgkm<C::MT + C::NT>();
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(af0, bf0);
+    __builtin_amdgcn_sched_barrier(0);
+    // F1's LDS reads must have landed before the barrier (after it, other
+    // waves refill stage kt's buffer); this wave's DMA of stage kt+1 must be
+    // done; stages kt+2 .. kt+NS-1 may stay in flight
+    use_regs<C::MT>(af1);
+    use_regs<C::NT>(bf1);
+    const int later = min(NS - 2, nk - 2 - kt);
+    if (NS >= 3 && later >= 1) {
+      if (NS >= 4 && later >= 2)
+        wait_vm<2 * C::LPW>();
+      else
+        wait_vm<C::LPW>();
+    } else {
+      wait_vm<0>();
     }
-    buf = buf == 2 ? 0 : buf + 1;
+    block_barrier();
+    if (kt + NS < nk) issue(buf, (kt + NS) * TBK);
+    const int nbuf = buf == NS - 1 ? 0 : buf + 1;
+    read_frags(af0, bf0, nbuf, 0);  // (stale and unused after the last step)
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(af1, bf1);
+    __builtin_amdgcn_sched_barrier(0);
+    buf = nbuf;
   }
   wait_vm_lgkm0<0>();
   block_barrier();  // every wave is done with the stages before the C tile reuses them
@@ -311,9 +375,9 @@ __device__ __forceinline__ void tiled_tile(const GroupedGemm& g, u32x4* smem, in
   __syncthreads();  // the next tile overwrites the LDS
 }
 
-template <bool SWIGLU, int BM, int BN, int WM, int WN, int OCC>
+template <bool SWIGLU, int BM, int BN, int WM, int WN, int NS, int OCC>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void ffn_tiled(GroupedGemm g, int n_tiles) {
-  using C = Tiled<SWIGLU, BM, BN, WM, WN>;
+  using C = Tiled<SWIGLU, BM, BN, WM, WN, NS>;
   __shared__ u32x4 smem[C::NSTAGE * C::STAGE];
   TileMap tm;
   tm.init(g.offsets, g.G, g.ident_rows, BM);
@@ -323,7 +387,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void ffn_tiled(GroupedGemm g, in
     const int n_tile = id / tm.total;
     int grp, row0, nrows;
     tm.find(id - n_tile * tm.total, grp, row0, nrows);
-    tiled_tile<SWIGLU, BM, BN, WM, WN>(g, smem, n_tile, grp, row0, nrows);
+    tiled_tile<SWIGLU, BM, BN, WM, WN, NS>(g, smem, n_tile, grp, row0, nrows);
   }
 }
 
@@ -360,10 +424,10 @@ static void launch_skinny(const GroupedGemm& g, hipStream_t s) {
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WN * WK), 0, s, g, nt);
 }
 
-template <bool SWIGLU, int BM, int BN, int WM, int WN, int OCC>
+template <bool SWIGLU, int BM, int BN, int WM, int WN, int NS, int OCC>
 static void launch_tiled(const GroupedGemm& g, hipStream_t s) {
   const int nt = g.N / (SWIGLU ? BN / 2 : BN);
-  auto k = ffn_tiled<SWIGLU, BM, BN, WM, WN, OCC>;
+  auto k = ffn_tiled<SWIGLU, BM, BN, WM, WN, NS, OCC>;
   const int grid = persistent_grid(k, 64 * WM * WN, tiles_bound(g, BM, nt));
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WM * WN), 0, s, g, nt);
 }
@@ -372,7 +436,7 @@ int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (small_m)
     launch_skinny<true, 1, 4, 4>(g, s);
   else
-    launch_tiled<true, 128, 256, 2, 4, 1>(g, s);
+    launch_tiled<true, 128, 256, 2, 4, 3, 1>(g, s);
   return launch_status();
 }
 
@@ -380,7 +444,7 @@ int launch_ffn_down_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (small_m)
     launch_skinny<false, 4, 1, 4>(g, s);
   else
-    launch_tiled<false, 128, 256, 2, 4, 1>(g, s);
+    launch_tiled<false, 128, 256, 2, 4, 3, 1>(g, s);
   return launch_status();
 }
 
