@@ -4,8 +4,42 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <unordered_map>
+
 #include "moe.h"
 #include "launch.hpp"
+
+namespace moe {
+
+int resident_grid(const void* kernel, int block, long long max_tiles) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int grid;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache[dev].find(kernel);
+    if (it != cache[dev].end()) {
+      grid = it->second;
+    } else {
+      int cus = 0, occ = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          cus <= 0)
+        cus = 256;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0) != hipSuccess ||
+          occ <= 0)
+        occ = 1;
+      grid = ((cus * occ + 7) / 8) * 8;
+      cache[dev][kernel] = grid;
+    }
+  }
+  const long long cap = ((max_tiles + 7) / 8) * 8;
+  return (int)(cap < grid ? cap : grid);
+}
+
+}  // namespace moe
 
 namespace {
 

@@ -394,22 +394,6 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void ffn_tiled(GroupedGemm g, in
 // ----------------------------------------------------------- launchers ----
 // Persistent grids: (resident blocks per CU) x (CUs), a multiple of 8, capped
 // by an upper bound of the tile count.
-template <typename Kern>
-static int persistent_grid(Kern kernel, int block, long long max_tiles) {
-  static int cache[64];  // per device
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] == 0) {
-    int cus = 0, occ = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0) != hipSuccess || occ <= 0)
-      occ = 1;
-    cache[dev] = ((cus * occ + 7) / 8) * 8;
-  }
-  long long cap = ((max_tiles + 7) / 8) * 8;
-  return (int)(cap < cache[dev] ? cap : cache[dev]);
-}
 
 static inline long long tiles_bound(const GroupedGemm& g, int BM, int n_tiles) {
   const int groups = g.offsets ? g.G : 1;
@@ -420,7 +404,7 @@ template <bool SWIGLU, int WN, int WK, int U>
 static void launch_skinny(const GroupedGemm& g, hipStream_t s) {
   const int nt = g.N / (16 * WN);
   auto k = ffn_skinny<SWIGLU, WN, WK, U>;
-  const int grid = persistent_grid(k, 64 * WN * WK, tiles_bound(g, 16, nt));
+  const int grid = resident_grid(reinterpret_cast<const void*>(k), 64 * WN * WK, tiles_bound(g, 16, nt));
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WN * WK), 0, s, g, nt);
 }
 
@@ -428,7 +412,7 @@ template <bool SWIGLU, int BM, int BN, int WM, int WN, int NS, int OCC>
 static void launch_tiled(const GroupedGemm& g, hipStream_t s) {
   const int nt = g.N / (SWIGLU ? BN / 2 : BN);
   auto k = ffn_tiled<SWIGLU, BM, BN, WM, WN, NS, OCC>;
-  const int grid = persistent_grid(k, 64 * WM * WN, tiles_bound(g, BM, nt));
+  const int grid = resident_grid(reinterpret_cast<const void*>(k), 64 * WM * WN, tiles_bound(g, BM, nt));
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WM * WN), 0, s, g, nt);
 }
 

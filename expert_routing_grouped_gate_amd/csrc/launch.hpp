@@ -11,6 +11,12 @@ namespace moe {
 // MOE_ERR_LAUNCH (-5) if the runtime reports a launch error, else 0.
 inline int launch_status() { return hipGetLastError() == hipSuccess ? 0 : -5; }
 
+// Blocks of `kernel` (launched with `block` threads) that are resident at
+// once on the current device: CUs x blocks per CU, rounded up to a multiple
+// of 8 and capped by max_tiles (rounded the same way).  The occupancy query
+// runs once per (kernel, device) and is cached.
+int resident_grid(const void* kernel, int block, long long max_tiles);
+
 int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
                          hipStream_t s);
 int launch_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,

@@ -136,8 +136,11 @@ __device__ __forceinline__ i32x8 ld32_fp8(const uint8_t* p) {
 
 // ---------------------------------------------------- GEMM1 (+SwiGLU) -----
 // Tile: 16 rows x 32 output columns (gate rows n0..n0+31 and up rows
-// I+n0..I+n0+31); WK waves split K and reduce through LDS.
-template <int WK>
+// I+n0..I+n0+31).  WK waves split K; each wave issues the loads of all S of
+// its 128-wide K steps before the first MFMA (the whole slice is one memory
+// round trip), then the waves reduce through LDS.  S == 0 selects a loop
+// over the steps for shapes without a fixed split.
+template <int WK, int S>
 __device__ __forceinline__ void mx_up_tile(const GroupedGemm& g, int lane, int wk, int n_tile,
                                            int grp, int row0, int nrows) {
   const int li = lane & 15, kb = lane >> 4;  // row in a 16-group, 32-block in a 128-step
@@ -149,43 +152,51 @@ __device__ __forceinline__ void mx_up_tile(const GroupedGemm& g, int lane, int w
   const uint8_t* xa = static_cast<const uint8_t*>(g.A) + (size_t)arow * K + kbeg + 16 * kb;
   const uint8_t* xs = g.A_scales + (size_t)arow * (K / 32) + kbeg / 32 + kb;
   const uint8_t* W = static_cast<const uint8_t*>(g.W) + (size_t)grp * g.w_gstride;
-  const uint8_t* S = g.W_scales + (size_t)grp * g.ws_gstride;
+  const uint8_t* Sc = g.W_scales + (size_t)grp * g.ws_gstride;
   const int rows4[4] = {n0 + li, n0 + 16 + li, g.up_off + n0 + li, g.up_off + n0 + 16 + li};
   const uint8_t* wp[4];
   const uint8_t* sp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     wp[j] = W + (size_t)rows4[j] * (K / 2) + (kbeg + 32 * kb) / 2;
-    sp[j] = S + (size_t)rows4[j] * (K / 32) + kbeg / 32 + kb;
+    sp[j] = Sc + (size_t)rows4[j] * (K / 32) + kbeg / 32 + kb;
   }
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nsteps = Kw / 128;
-  for (int st = 0; st < nsteps; st += 2) {
-    const int nu = min(2, nsteps - st);
-    u32x4 wa[2][4];
-    uint32_t ws[2][4], xsc[2];
-    i32x8 xb[2];
+  if (S > 0) {
+    u32x4 wa[S > 0 ? S : 1][4];
+    uint32_t ws[S > 0 ? S : 1][4], xsc[S > 0 ? S : 1];
+    i32x8 xb[S > 0 ? S : 1];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (u < nu) {
-        const int s = st + u;
+    for (int st = 0; st < S; ++st) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          wa[u][j] = ld16_stream(wp[j] + s * 64);
-          ws[u][j] = sp[j][s * 4];
-        }
-        xb[u] = ld32_fp8(xa + s * 128);
-        xsc[u] = xs[s * 4];
+      for (int j = 0; j < 4; ++j) {
+        wa[st][j] = ld16_stream(wp[j] + st * 64);
+        ws[st][j] = sp[j][st * 4];
       }
+      xb[st] = ld32_fp8(xa + st * 128);
+      xsc[st] = xs[st * 4];
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      if (u < nu) {
+    for (int st = 0; st < S; ++st)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = mfma_fp4_fp8(wa[u][j], xb[u], ws[u][j], xsc[u], acc[j]);
+      for (int j = 0; j < 4; ++j) acc[j] = mfma_fp4_fp8(wa[st][j], xb[st], ws[st][j], xsc[st], acc[j]);
+  } else {
+    const int nsteps = Kw / 128;
+    for (int st = 0; st < nsteps; ++st) {
+      u32x4 wa[4];
+      uint32_t ws[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wa[j] = ld16_stream(wp[j] + st * 64);
+        ws[j] = sp[j][st * 4];
       }
+      const i32x8 xb = ld32_fp8(xa + st * 128);
+      const uint32_t xsc = xs[st * 4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = mfma_fp4_fp8(wa[j], xb, ws[j], xsc, acc[j]);
+    }
   }
   if (WK > 1) {
     __shared__ f32x4 red[WK > 1 ? WK - 1 : 1][4][64];
@@ -232,7 +243,7 @@ __device__ __forceinline__ void mx_up_tile(const GroupedGemm& g, int lane, int w
   }
 }
 
-template <int WK>
+template <int WK, int S>
 __global__ __launch_bounds__(64 * WK) void ffn_mx_up(GroupedGemm g, int n_tiles) {
   const int lane = threadIdx.x & 63, wk = threadIdx.x >> 6;
   TileMap tm;
@@ -243,20 +254,24 @@ __global__ __launch_bounds__(64 * WK) void ffn_mx_up(GroupedGemm g, int n_tiles)
     const int n_tile = id / tm.total;
     int grp, row0, nrows;
     tm.find(id - n_tile * tm.total, grp, row0, nrows);
-    mx_up_tile<WK>(g, lane, wk, n_tile, grp, row0, nrows);
+    mx_up_tile<WK, S>(g, lane, wk, n_tile, grp, row0, nrows);
   }
 }
 
 // ------------------------------------------------------------- GEMM2 -----
-// Tile: 16 rows x 16*WN output columns; wave wn streams 16 rows of w2.
-template <int WN>
-__global__ __launch_bounds__(64 * WN) void ffn_mx_down(GroupedGemm g, int n_tiles) {
-  const int lane = threadIdx.x & 63, wn = threadIdx.x >> 6;
+// Tile: 16 rows x 16*WN output columns; wave (wn, wk) streams 16 rows of w2
+// over K slice wk (all S steps loaded at once when S > 0), then the WK
+// partial sums of each column group are reduced through LDS.
+template <int WN, int WK, int S>
+__global__ __launch_bounds__(64 * WN * WK) void ffn_mx_down(GroupedGemm g, int n_tiles) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave % WN, wk = wave / WN;
   const int li = lane & 15, kb = lane >> 4;
   TileMap tm;
   tm.init(g.offsets, g.G, g.ident_rows, 16);
   const int total = tm.total * n_tiles;
   const int K = g.K;
+  const int Kw = K / WK, kbeg = wk * Kw;
   for (int t = blockIdx.x; t < total; t += gridDim.x) {
     const int id = xcd_remap(t, total);
     const int n_tile = id / tm.total;
@@ -264,30 +279,41 @@ __global__ __launch_bounds__(64 * WN) void ffn_mx_down(GroupedGemm g, int n_tile
     tm.find(id - n_tile * tm.total, grp, row0, nrows);
     const int n0 = n_tile * 16 * WN + wn * 16;
     const int r = row0 + min(li, nrows - 1);
-    const uint8_t* xa = static_cast<const uint8_t*>(g.A) + (size_t)r * K + 16 * kb;
-    const uint8_t* xs = g.A_scales + (size_t)r * (K / 32) + kb;
+    const uint8_t* xa = static_cast<const uint8_t*>(g.A) + (size_t)r * K + kbeg + 16 * kb;
+    const uint8_t* xs = g.A_scales + (size_t)r * (K / 32) + kbeg / 32 + kb;
     const uint8_t* wp = static_cast<const uint8_t*>(g.W) + (size_t)grp * g.w_gstride +
-                        (size_t)(n0 + li) * (K / 2) + 16 * kb;
-    const uint8_t* sp = g.W_scales + (size_t)grp * g.ws_gstride + (size_t)(n0 + li) * (K / 32) + kb;
+                        (size_t)(n0 + li) * (K / 2) + (kbeg + 32 * kb) / 2;
+    const uint8_t* sp = g.W_scales + (size_t)grp * g.ws_gstride + (size_t)(n0 + li) * (K / 32) +
+                        kbeg / 32 + kb;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int nsteps = K / 128;
-    for (int st = 0; st < nsteps; st += 4) {
-      const int nu = min(4, nsteps - st);
-      u32x4 wa[4];
-      uint32_t ws[4], xsc[4];
-      i32x8 xb[4];
+    if (S > 0) {
+      u32x4 wa[S > 0 ? S : 1];
+      uint32_t ws[S > 0 ? S : 1], xsc[S > 0 ? S : 1];
+      i32x8 xb[S > 0 ? S : 1];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u < nu) {
-          const int s = st + u;
-          wa[u] = ld16_stream(wp + s * 64);
-          ws[u] = sp[s * 4];
-          xb[u] = ld32_fp8(xa + s * 128);
-          xsc[u] = xs[s * 4];
-        }
+      for (int u = 0; u < S; ++u) {
+        wa[u] = ld16_stream(wp + u * 64);
+        ws[u] = sp[u * 4];
+        xb[u] = ld32_fp8(xa + u * 128);
+        xsc[u] = xs[u * 4];
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u < nu) acc = mfma_fp4_fp8(wa[u], xb[u], ws[u], xsc[u], acc);
+      for (int u = 0; u < S; ++u) acc = mfma_fp4_fp8(wa[u], xb[u], ws[u], xsc[u], acc);
+    } else {
+      const int nsteps = Kw / 128;
+      for (int u = 0; u < nsteps; ++u)
+        acc = mfma_fp4_fp8(ld16_stream(wp + u * 64), ld32_fp8(xa + u * 128), sp[u * 4], xs[u * 4], acc);
+    }
+    if (WK > 1) {
+      __shared__ f32x4 red[WK > 1 ? WK - 1 : 1][WN][64];
+      if (wk > 0) red[wk - 1][wn][lane] = acc;
+      __syncthreads();
+      if (wk == 0) {
+#pragma unroll
+        for (int w = 0; w < WK - 1; ++w) acc += red[w][wn][lane];
+      }
+      __syncthreads();
+      if (wk != 0) continue;
     }
     if (li < nrows) {
       const int nc = n0 + 4 * kb;
@@ -300,51 +326,63 @@ __global__ __launch_bounds__(64 * WN) void ffn_mx_down(GroupedGemm g, int n_tile
 }
 
 // ----------------------------------------------------------- launchers ----
-template <typename Kern>
-static int mx_grid(Kern kernel, int block, long long max_tiles) {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] == 0) {
-    int cus = 0, occ = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0) != hipSuccess || occ <= 0)
-      occ = 1;
-    cache[dev] = ((cus * occ + 7) / 8) * 8;
-  }
-  const long long cap = ((max_tiles + 7) / 8) * 8;
-  return (int)(cap < cache[dev] ? cap : cache[dev]);
-}
 
 static inline long long mx_tiles_bound(const GroupedGemm& g, int n_tiles) {
   const int groups = g.offsets ? g.G : 1;
   return ((long long)(g.total_rows + 15) / 16 + groups) * n_tiles;
 }
 
-template <int WK>
+template <int WK, int S>
 static void launch_mx_up(const GroupedGemm& g, hipStream_t s) {
   const int nt = g.N / 32;
-  auto k = ffn_mx_up<WK>;
-  const int grid = mx_grid(k, 64 * WK, mx_tiles_bound(g, nt));
+  auto k = ffn_mx_up<WK, S>;
+  const int grid = resident_grid(reinterpret_cast<const void*>(k), 64 * WK, mx_tiles_bound(g, nt));
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WK), 0, s, g, nt);
 }
 
+// K = H: 128-wide steps split over WK waves, S steps each (all in flight).
 int launch_ffn_up_w4a8(const GroupedGemm& g, hipStream_t s) {
-  // waves split K in 128-wide steps: 4 waves need K % 512 == 0
-  if (g.K % 512 == 0)
-    launch_mx_up<4>(g, s);
+  const int steps = g.K / 128;
+  if (steps == 32)
+    launch_mx_up<8, 4>(g, s);
+  else if (steps == 16)
+    launch_mx_up<4, 4>(g, s);
+  else if (steps == 8)
+    launch_mx_up<2, 4>(g, s);
+  else if (steps == 4)
+    launch_mx_up<1, 4>(g, s);
+  else if (steps == 2)
+    launch_mx_up<1, 2>(g, s);
+  else if (steps % 4 == 0)
+    launch_mx_up<4, 0>(g, s);
   else
-    launch_mx_up<1>(g, s);
+    launch_mx_up<1, 0>(g, s);
   return launch_status();
 }
 
-int launch_ffn_down_w4a8(const GroupedGemm& g, hipStream_t s) {
-  constexpr int WN = 4;
+template <int WN, int WK, int S>
+static void launch_mx_down(const GroupedGemm& g, hipStream_t s) {
   const int nt = g.N / (16 * WN);
-  auto k = ffn_mx_down<WN>;
-  const int grid = mx_grid(k, 64 * WN, mx_tiles_bound(g, nt));
-  hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WN), 0, s, g, nt);
+  auto k = ffn_mx_down<WN, WK, S>;
+  const int grid = resident_grid(reinterpret_cast<const void*>(k), 64 * WN * WK, mx_tiles_bound(g, nt));
+  hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WN * WK), 0, s, g, nt);
+}
+
+// K = I: same idea; N = H is a multiple of 64.
+int launch_ffn_down_w4a8(const GroupedGemm& g, hipStream_t s) {
+  const int steps = g.K / 128;
+  if (steps == 12)
+    launch_mx_down<4, 1, 12>(g, s);
+  else if (steps == 8)
+    launch_mx_down<2, 2, 4>(g, s);
+  else if (steps == 4)
+    launch_mx_down<4, 1, 4>(g, s);
+  else if (steps == 2)
+    launch_mx_down<4, 1, 2>(g, s);
+  else if (steps == 1)
+    launch_mx_down<4, 1, 1>(g, s);
+  else
+    launch_mx_down<4, 1, 0>(g, s);
   return launch_status();
 }
 
