@@ -135,6 +135,44 @@ struct TileMap {
     row0 = __shfl(r0, src, 64);
     nrows = __shfl(nr, src, 64);
   }
+
+  // The group owning m-tile q: its index, first m-tile, m-tile count, first
+  // row and end row.
+  __device__ __forceinline__ void find_group(int q, int& g_out, int& first_mt, int& n_mt,
+                                             int& grow0, int& grow1) const {
+    if (offsets == nullptr) {
+      g_out = 0;
+      first_mt = 0;
+      n_mt = total;
+      grow0 = 0;
+      grow1 = ident_rows;
+      return;
+    }
+    const int lane = threadIdx.x & 63;
+    const bool mine = q >= excl && q < excl + (tiles[0] + tiles[1] + tiles[2] + tiles[3] + tiles[4]);
+    const unsigned long long bal = __ballot(mine);
+    const int src = __ffsll((long long)bal) - 1;
+    int g = 0, f = 0, n = 0, a = 0, b = 0;
+    if (lane == src) {
+      int s = excl;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        if (q >= s && q < s + tiles[i]) {
+          g = gbeg + i;
+          f = s;
+          n = tiles[i];
+          a = o[i];
+          b = o[i + 1];
+        }
+        s += tiles[i];
+      }
+    }
+    g_out = __shfl(g, src, 64);
+    first_mt = __shfl(f, src, 64);
+    n_mt = __shfl(n, src, 64);
+    grow0 = __shfl(a, src, 64);
+    grow1 = __shfl(b, src, 64);
+  }
 };
 
 }  // namespace moe
