@@ -43,7 +43,85 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times) and "
                          "exit: the reference for scaling HBM byte counters")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print the HBM-counter summary (markdown) of a rocprofv3 --pmc FETCH_SIZE / "
+                         "WRITE_SIZE pair of runs of this bench and of --calibrate-copy-mib 1024, and exit")
     return ap.parse_args()
+
+
+COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_counters_qwen3_decode_T16_E128.md")
+GEMM1_SOURCES = ("expert_routing_grouped_gate_amd/csrc/ffn_bf16.hip",
+                 "expert_routing_grouped_gate_amd/csrc/common.hpp")
+GEMM1_KERNEL = "ffn_skinny<true"
+
+
+def gemm1_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM1_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_means(path):
+    import collections
+    import csv
+    d = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in d.items()}
+
+
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Markdown summary of HBM byte counters per kernel, scaled by what the
+    same counters read for a plain 1 GiB device copy."""
+    fetch, write = _counter_means(fetch_csv), _counter_means(write_csv)
+    cf = max(v for k, v in _counter_means(copy_fetch_csv).items() if "copyBuffer" in k)
+    cw = max(v for k, v in _counter_means(copy_write_csv).items() if "copyBuffer" in k)
+    kib = 1024 * 1024  # the copy moves 1 GiB = 1,048,576 KiB each way
+    sf, sw = kib / cf, kib / cw
+    lines = [f"# HBM byte counters, Qwen3-style decode layer (T=16, H=4096, E=128, top-8, I=1536, bf16)", "",
+             "Each counter in its own pass (run from /tmp on one MI355X, repo at $R):", "", "```",
+             "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_fetch_decode -o run --output-format csv -- python $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_write_decode -o run --output-format csv -- python $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_fetch_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
+             "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_write_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
+             "python $R/bench.py --summarize-counters <the four run_counter_collection.csv files>", "```", "",
+             f"Calibration (1 GiB device copy): FETCH_SIZE {cf:,.1f} KiB -> scale x{sf:.3f}; "
+             f"WRITE_SIZE {cw:,.1f} KiB -> scale x{sw:.3f}.", "",
+             "| kernel | FETCH_SIZE KiB | read bytes (scaled) | WRITE_SIZE KiB | written bytes (scaled) |",
+             "|---|---|---|---|---|"]
+    g1 = None
+    for k in sorted(fetch, key=lambda k: -fetch[k]):
+        if not k.startswith(("void moe::", "moe::")):
+            continue
+        rb, wb = fetch[k] * sf * 1024, write.get(k, 0.0) * sw * 1024
+        lines.append(f"| `{k[:80]}` | {fetch[k]:,.1f} | {rb / 1e9:.4f} GB | {write.get(k, 0.0):,.1f} | {wb / 1e6:.3f} MB |")
+        if GEMM1_KERNEL in k:
+            g1 = (rb, wb)
+    lines += ["", "Machine-readable (bench.py reports `roofline.traffic` from these only while the GEMM1 "
+              "sources still hash to the value below):", "",
+              f"gemm1_source_sha256_16: {gemm1_source_hash()}",
+              f"gemm1_read_bytes: {int(g1[0]) if g1 else 0}",
+              f"gemm1_write_bytes: {int(g1[1]) if g1 else 0}", ""]
+    print("\n".join(lines))
+
+
+def measured_gemm1_traffic():
+    """HBM bytes per GEMM1 launch from the committed counter summary, or None
+    when it is missing or was taken on different GEMM1 sources."""
+    try:
+        kv = {}
+        for line in open(COUNTERS_MD):
+            if ":" in line and line.split(":")[0].strip() in ("gemm1_source_sha256_16", "gemm1_read_bytes", "gemm1_write_bytes"):
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+        if kv.get("gemm1_source_sha256_16") != gemm1_source_hash():
+            return None
+        return int(kv["gemm1_read_bytes"]) + int(kv["gemm1_write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def calibrate_copy(mib: int):
@@ -121,6 +199,9 @@ def cpu_baseline(cfg, cpu, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -180,8 +261,9 @@ def main():
     layer_gbs = wl["layer_bytes"] / (ms * 1e-3) / 1e9
     layer_tflops = wl["flops"] / (ms * 1e-3) / 1e12
     if decode or cfg.fmt == "w4a8":
+        traffic = measured_gemm1_traffic() if cfg.name == "qwen3_decode" else None
         roof = {"bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
         g1_tf = wl["g1_flops"] / (g1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(g1_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
