@@ -309,7 +309,7 @@ __device__ __forceinline__ void tiled_tile(const GroupedGemm& g, u32x4* smem, in
     // F0 was requested before F1 and LDS reads complete in order: waiting
     // until at most F1's reads are pending leaves those in flight during the
     // MFMAs below
-    wait_lgkm<C::MT + C::NT>();
+    wait_lgkm<(C::MT + C::NT < 15 ? C::MT + C::NT : 15)>();
     __builtin_amdgcn_sched_barrier(0);
     mfmas(af0, bf0);
     __builtin_amdgcn_sched_barrier(0);

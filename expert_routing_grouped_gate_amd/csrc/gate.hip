@@ -115,16 +115,18 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
   const int lrow = tid >> 2, lch = tid & 3;
   const uint16_t* xp = x + (size_t)min(t0 + (lrow & 31), T - 1) * H + lch * 8;
   const float* wp = wr + (size_t)min(e0 + lrow, E - 1) * H + lch * 8;
-  u32x4 rx;
-  float rw[8];
-  auto gload = [&](int k0) {
+  // two register sets: step k+2 is loaded while step k computes and step k+1
+  // waits to be split and stored into the other LDS buffer
+  u32x4 rx0, rx1;
+  float rw0[8], rw1[8];
+  auto gload = [&](u32x4& rx, float* rw, int k0) {
     if (tid < 128) rx = ld16(xp + k0);
     const float4 a = *reinterpret_cast<const float4*>(wp + k0);
     const float4 b = *reinterpret_cast<const float4*>(wp + k0 + 4);
     rw[0] = a.x; rw[1] = a.y; rw[2] = a.z; rw[3] = a.w;
     rw[4] = b.x; rw[5] = b.y; rw[6] = b.z; rw[7] = b.w;
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const u32x4& rx, const float* rw, int buf) {
     if (tid < 128) xs[buf][lrow * 4 + lch] = rx;
     u32x4 h, m, l;
     split3_bf16(rw, h, m, l);
@@ -134,13 +136,7 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
   };
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fc = lane >> 4;
-  const int nk = H / 32;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * 32);
+  auto compute = [&](int buf) {
     const u32x4 a0 = xs[buf][fr * 4 + fc];
     const u32x4 a1 = xs[buf][(16 + fr) * 4 + fc];
 #pragma unroll
@@ -149,7 +145,21 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
       acc0 = mfma16x16x32(a0, b, acc0);
       acc1 = mfma16x16x32(a1, b, acc1);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+  };
+  const int nk = H / 32;
+  gload(rx0, rw0, 0);
+  if (nk > 1) gload(rx1, rw1, 32);
+  lstore(rx0, rw0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    if (kt + 2 < nk) gload(rx0, rw0, (kt + 2) * 32);
+    compute(0);
+    if (kt + 1 < nk) lstore(rx1, rw1, 1);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    if (kt + 3 < nk) gload(rx1, rw1, (kt + 3) * 32);
+    compute(1);
+    if (kt + 2 < nk) lstore(rx0, rw0, 0);
     __syncthreads();
   }
   // D[m][n]: lane holds expert 16*wave + (lane & 15), tokens 4*(lane>>4) + i

@@ -16,7 +16,7 @@
 
 namespace moe {
 
-constexpr int RCHUNK = 2048;
+constexpr int RCHUNK = 1024;
 constexpr int RSUB = RCHUNK / 256;
 
 size_t route_workspace_bytes(int T, int k, int E) {

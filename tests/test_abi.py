@@ -77,7 +77,7 @@ def test_gate_topk_checks(lib):
 
 def test_route_checks_and_workspace(lib):
     assert lib.moe_route_workspace_size(16, 8, 128) == 0           # one chunk
-    assert lib.moe_route_workspace_size(4096, 8, 192) == 16 * 193 * 4
+    assert lib.moe_route_workspace_size(4096, 8, 192) == 32 * 193 * 4   # 1024-pair chunks
     f = lib.moe_route
     assert f(FAKE, 4096, 8, 192, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == WS
     assert f(FAKE, 4096, 8, 192, FAKE, FAKE, FAKE, FAKE, None, FAKE, 100, None) == WS

@@ -117,3 +117,32 @@ def test_mx_layer_small(name):
 
 def test_mx_layer_full_decode():
     _layer_check(CFG["qwen3_decode_w4a8"])
+
+
+def test_mx_layer_deterministic_and_graph_capture():
+    L = get_layer(SMALL["mx_mid"])
+    layer = L.layer()
+    x = L.dev["x"]
+    eager = layer.forward(x).clone()
+    assert torch.equal(layer.forward(x), eager)
+    out = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(x, out)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward(x, out)
+    for i in range(3):
+        out.fill_(0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        layer.forward(x)
+        torch.cuda.synchronize()
+
+
+def test_mx_quantize_zero_rows():
+    codes, scales = B.mx_quantize(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"))
+    assert codes.shape == (0, 64) and scales.shape == (0, 2)

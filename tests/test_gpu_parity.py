@@ -273,3 +273,59 @@ FULL = [("qwen3_decode", None), ("qwen3_prefill", [0, 1, 2, 777, 2048, 4094, 409
 @pytest.mark.parametrize("name,tokens", FULL, ids=[f[0] for f in FULL])
 def test_layer_full_size(name, tokens):
     _layer_check(CFG[name], tokens)
+
+
+# ------------------------------------------------------- degenerate cases --
+
+DEGENERATE = {
+    # every token selects every expert (k = E): routing is a dense copy
+    "k_eq_E": CFG["tiny"].with_(name="k_eq_E", T=37, E=8, k=8, x_seed=31),
+    # one expert, one slot: the layer is a plain SwiGLU MLP (softmax weight 1)
+    "one_expert": CFG["tiny"].with_(name="one_expert", T=50, E=1, k=1, x_seed=32, family_seed=1031),
+    # a wider hidden size than the model configs, several K tiles of every kernel
+    "wide_H": CFG["tiny"].with_(name="wide_H", T=24, H=8192, E=4, k=2, I=256, x_seed=33, family_seed=1033),
+    # sigmoid gating with a shared expert and many tokens per expert (tiled path)
+    "hy3_dense": CFG["hy3"].with_(name="hy3_dense", T=520, H=512, E=6, k=3, I=128, shared_I=256,
+                                  x_seed=34, family_seed=1034),
+}
+
+
+@pytest.mark.parametrize("name", list(DEGENERATE))
+def test_layer_degenerate(name):
+    _layer_check(DEGENERATE[name])
+
+
+def test_one_expert_layer_is_the_plain_mlp():
+    L = get_layer(DEGENERATE["one_expert"])
+    out = L.layer().forward(L.dev["x"])
+    ref = mx.bf16_round(moe.expert_ffn(L.x64(), *L.expert(0)))
+    assert_close_bf16(bf16_np(out), ref, ATOL, RTOL, "one expert")
+
+
+def test_all_tokens_on_one_expert():
+    """A router bias that makes expert 3 win for every token: one group holds
+    all rows, the others none (ragged extreme)."""
+    cfg = CFG["tiny"].with_(name="skew", T=300, E=8, k=1, x_seed=35)
+    L = get_layer(cfg)
+    bias = torch.zeros(cfg.E)
+    bias[3] = 1000.0
+    layer = B.MoeLayer(L.weights, L.dev["wr"], cfg.k, B.GATE_SOFTMAX, bias.cuda())
+    out = layer.forward(L.dev["x"])
+    torch.cuda.synchronize()
+    counts = to_np(layer.buf["counts"])
+    assert counts[3] == cfg.T and counts.sum() == cfg.T
+    ref = mx.bf16_round(moe.expert_ffn(L.x64(), *L.expert(3)))  # softmax over one slot: weight 1
+    assert_close_bf16(bf16_np(out), ref, ATOL, RTOL, "all on expert 3")
+
+
+def test_zero_tokens_every_entry_point():
+    L = get_layer(SMALL["tiny"])
+    cfg = L.cfg
+    x0 = L.dev["x"][:0]
+    assert B.router_logits(x0, L.dev["wr"]).shape == (0, cfg.E)
+    ids, w = B.gate_topk(torch.empty((0, cfg.E), device="cuda"), cfg.k, B.GATE_SOFTMAX)
+    counts, offsets, sp, pp = B.route(ids, cfg.E)   # T = 0: nothing is enqueued
+    act, _ = B.grouped_ffn_up(L.weights, x0, None, cfg.k, sp, offsets)
+    y = B.grouped_ffn_down(L.weights, act, None, 0, cfg.k, offsets)
+    assert B.combine(y, pp, w, None).shape == (0, cfg.H)
+    torch.cuda.synchronize()
