@@ -97,6 +97,10 @@ int check_weights(const MoeFfnWeights* w) {
     if (w->shared_I > 0 &&
         (st = check_ptrs({w->shared_w13, w->shared_w13_scales, w->shared_w2, w->shared_w2_scales})))
       return st;
+    // one expert's E2M1 matrix (2I x H/2 bytes, H x I/2 for w2) is addressed
+    // with 32-bit offsets
+    const long long big = (long long)(w->I > w->shared_I ? w->I : w->shared_I) * w->H;
+    if (big >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
   }
   return MOE_ERR_UNSUPPORTED;

@@ -15,9 +15,9 @@
 // integer-exact (no hardware convert), so codes are reproducible bit for bit.
 //
 // S0 (mx_quant): four lanes per 32-block, 8 elements per lane.
-// S5/S6 (ffn_mx_up / ffn_mx_down): the skinny weight-streaming tiles of the
-// bf16 path with v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 weights as the A
-// operand, E4M3 activations as B).  Operand layout of one 128-wide K step,
+// S5/S6 (ffn_mx_stream): weight-streaming grouped GEMMs on
+// v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 weights as the A operand, E4M3
+// activations as B), one wave per 16-row tile.  Operand layout of one 128-wide K step,
 // lane l = 16*g + i (row or column i, g = 0..3), measured on gfx950:
 //   E2M1: 16 bytes holding k = 32g .. 32g+31, low nibble = even k;
 //   E4M3: bytes 0-15 hold k = 16g .. 16g+15, bytes 16-31 hold
@@ -134,194 +134,209 @@ __device__ __forceinline__ i32x8 ld32_fp8(const uint8_t* p) {
   return r;
 }
 
-// ---------------------------------------------------- GEMM1 (+SwiGLU) -----
-// Tile: 16 rows x 32 output columns (gate rows n0..n0+31 and up rows
-// I+n0..I+n0+31).  WK waves split K; each wave issues the loads of all S of
-// its 128-wide K steps before the first MFMA (the whole slice is one memory
-// round trip), then the waves reduce through LDS.  S == 0 selects a loop
-// over the steps for shapes without a fixed split.
-template <int WK, int S>
-__device__ __forceinline__ void mx_up_tile(const GroupedGemm& g, int lane, int wk, int n_tile,
-                                           int grp, int row0, int nrows) {
-  const int li = lane & 15, kb = lane >> 4;  // row in a 16-group, 32-block in a 128-step
-  const int n0 = n_tile * 32;
-  const int K = g.K;
-  const int r = row0 + min(li, nrows - 1);
+// ------------------------------------------------ streaming W4A8 GEMMs ---
+// One wave owns a whole tile (16 activation rows x 4 groups of 16 weight
+// rows, the full K) and walks its tiles as one sequence of U-step batches,
+// double-buffered in registers: the loads of the next batch, which may be the
+// first batch of the wave's next tile, are issued before the MFMAs of the
+// current one.  The weight stream of a wave therefore does not pause at tile
+// boundaries, and no LDS, barrier or cross-wave reduction is involved.
+// GEMM1 (SWIGLU): groups = gate rows n0.., n0+16.., up rows I+n0.., I+n0+16..
+// (32 output columns, one MX block of the quantised output).  GEMM2: groups =
+// rows n0 + 16j (64 output columns).
+struct MxTile {
+  int grp, n0, row0, nrows;  // wave-uniform (scalar registers)
+  int live;                  // 0: no tile (its weight loads read nothing)
+  const uint8_t* xa;         // this lane's activation row, + 16*kb
+  const uint8_t* xs;         // this lane's activation scale row
+};
+
+template <bool SWIGLU>
+__device__ __forceinline__ MxTile mx_tile_at(const GroupedGemm& g, const TileMap& tm, int id,
+                                             int li, int kb) {
+  MxTile t;
+  const int n_tile = id / tm.total;
+  int grp, row0, nrows;
+  tm.find(id - n_tile * tm.total, grp, row0, nrows);
+  t.grp = __builtin_amdgcn_readfirstlane(grp);
+  t.row0 = __builtin_amdgcn_readfirstlane(row0);
+  t.nrows = __builtin_amdgcn_readfirstlane(nrows);
+  t.n0 = __builtin_amdgcn_readfirstlane(n_tile * (SWIGLU ? 32 : 64));
+  const int r = t.row0 + min(li, t.nrows - 1);  // rows past the tile end reuse a valid row
   const int arow = g.gather ? g.sorted_pair[r] / g.topk : r;
-  const int Kw = K / WK, kbeg = wk * Kw;
-  const uint8_t* xa = static_cast<const uint8_t*>(g.A) + (size_t)arow * K + kbeg + 16 * kb;
-  const uint8_t* xs = g.A_scales + (size_t)arow * (K / 32) + kbeg / 32 + kb;
-  const uint8_t* W = static_cast<const uint8_t*>(g.W) + (size_t)grp * g.w_gstride;
-  const uint8_t* Sc = g.W_scales + (size_t)grp * g.ws_gstride;
-  const int rows4[4] = {n0 + li, n0 + 16 + li, g.up_off + n0 + li, g.up_off + n0 + 16 + li};
-  const uint8_t* wp[4];
-  const uint8_t* sp[4];
+  t.xa = static_cast<const uint8_t*>(g.A) + (size_t)arow * g.K + 16 * kb;
+  t.xs = g.A_scales + (size_t)arow * (g.K / 32);
+  t.live = 1;
+  return t;
+}
+
+template <int U>
+struct MxBatch {
+  u32x4 w[U][4];      // E2M1 weights, 32 k per lane
+  i32x8 x[U];         // E4M3 activations, 32 k per lane
+  uint32_t ws[U][4];  // 4 scale bytes per word; this lane's is byte kb
+  uint32_t xs[U];
+};
+
+// First row of weight group j (uniform); the lane adds li.
+template <bool SWIGLU>
+__device__ __forceinline__ int mx_wrow0(const GroupedGemm& g, int n0, int j) {
+  if (SWIGLU) return (j >= 2 ? g.up_off : 0) + n0 + 16 * (j & 1);
+  return n0 + 16 * j;
+}
+
+// Raw buffer descriptor over [p, p + bytes): loads address it as a uniform
+// base (scalar registers) plus a 32-bit lane offset and a scalar offset.
+// Word 3 = 0x00020000: the raw (untyped, stride 0) dword format on gfx9.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Batch of U K-steps (128 each) starting at step st0 of tile t.  Weights and
+// their scales are read through buffer descriptors over the expert's matrix:
+// the lane offset (woff = li*K/2 + 16*kb, soff = li*K/32) is the same for
+// every tile and every step, the row group and step go into the scalar
+// offset, so the weight stream needs no per-tile vector address registers.
+template <bool SWIGLU, int U>
+__device__ __forceinline__ void mx_load(MxBatch<U>& b, const GroupedGemm& g, const MxTile& t,
+                                        int st0, uint32_t woff, uint32_t soff) {
+  const int K = g.K;
+  // a dead tile gets empty descriptors: its loads return zeros without a
+  // memory access
+  const uint32_t wrows = SWIGLU ? 2u * (uint32_t)g.up_off : (uint32_t)g.N;  // rows of one matrix
+  const __amdgpu_buffer_rsrc_t wr =
+      mx_rsrc(static_cast<const uint8_t*>(g.W) + (size_t)t.grp * g.w_gstride,
+              t.live ? wrows * (uint32_t)(K / 2) : 0u);
+  const __amdgpu_buffer_rsrc_t sr = mx_rsrc(g.W_scales + (size_t)t.grp * g.ws_gstride,
+                                            t.live ? wrows * (uint32_t)(K / 32) : 0u);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    wp[j] = W + (size_t)rows4[j] * (K / 2) + (kbeg + 32 * kb) / 2;
-    sp[j] = Sc + (size_t)rows4[j] * (K / 32) + kbeg / 32 + kb;
-  }
-  f32x4 acc[4];
+    const int row0 = mx_wrow0<SWIGLU>(g, t.n0, j);
+    const int wso = row0 * (K / 2) + st0 * 64;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (S > 0) {
-    u32x4 wa[S > 0 ? S : 1][4];
-    uint32_t ws[S > 0 ? S : 1][4], xsc[S > 0 ? S : 1];
-    i32x8 xb[S > 0 ? S : 1];
-#pragma unroll
-    for (int st = 0; st < S; ++st) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wa[st][j] = ld16_stream(wp[j] + st * 64);
-        ws[st][j] = sp[j][st * 4];
-      }
-      xb[st] = ld32_fp8(xa + st * 128);
-      xsc[st] = xs[st * 4];
-    }
-#pragma unroll
-    for (int st = 0; st < S; ++st)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = mfma_fp4_fp8(wa[st][j], xb[st], ws[st][j], xsc[st], acc[j]);
-  } else {
-    const int nsteps = Kw / 128;
-    for (int st = 0; st < nsteps; ++st) {
-      u32x4 wa[4];
-      uint32_t ws[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wa[j] = ld16_stream(wp[j] + st * 64);
-        ws[j] = sp[j][st * 4];
-      }
-      const i32x8 xb = ld32_fp8(xa + st * 128);
-      const uint32_t xsc = xs[st * 4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = mfma_fp4_fp8(wa[j], xb, ws[j], xsc, acc[j]);
-    }
-  }
-  if (WK > 1) {
-    __shared__ f32x4 red[WK > 1 ? WK - 1 : 1][4][64];
-    if (wk > 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) red[wk - 1][j][lane] = acc[j];
-    }
-    __syncthreads();
-    if (wk != 0) {
-      __syncthreads();
-      return;
-    }
-#pragma unroll
-    for (int w = 0; w < WK - 1; ++w)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += red[w][j][lane];
-    __syncthreads();
-  }
-  // D[n][m]: lane holds token li, columns n0 + 4*kb + i (lo) and n0 + 16 + 4*kb + i (hi)
-  float a[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[i] = (acc[0][i] / (1.f + expf(-acc[0][i]))) * acc[2][i];
-    a[4 + i] = (acc[1][i] / (1.f + expf(-acc[1][i]))) * acc[3][i];
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
-  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-  const int e = mx_exponent(amax);
-  const float inv = exp2_neg(e);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo |= e4m3_encode(a[i] * inv) << (8 * i);
-    hi |= e4m3_encode(a[4 + i] * inv) << (8 * i);
-  }
-  if (li < nrows) {
-    uint8_t* orow = static_cast<uint8_t*>(g.out) + (size_t)(row0 + li) * g.N;
-    *reinterpret_cast<uint32_t*>(orow + n0 + 4 * kb) = lo;
-    *reinterpret_cast<uint32_t*>(orow + n0 + 16 + 4 * kb) = hi;
-    if (kb == 0) g.out_scales[(size_t)(row0 + li) * (g.N / 32) + n0 / 32] = (uint8_t)(e + 127);
-  }
-}
-
-template <int WK, int S>
-__global__ __launch_bounds__(64 * WK) void ffn_mx_up(GroupedGemm g, int n_tiles) {
-  const int lane = threadIdx.x & 63, wk = threadIdx.x >> 6;
-  TileMap tm;
-  tm.init(g.offsets, g.G, g.ident_rows, 16);
-  const int total = tm.total * n_tiles;
-  for (int t = blockIdx.x; t < total; t += gridDim.x) {
-    const int id = xcd_remap(t, total);
-    const int n_tile = id / tm.total;
-    int grp, row0, nrows;
-    tm.find(id - n_tile * tm.total, grp, row0, nrows);
-    mx_up_tile<WK, S>(g, lane, wk, n_tile, grp, row0, nrows);
-  }
-}
-
-// ------------------------------------------------------------- GEMM2 -----
-// Tile: 16 rows x 16*WN output columns; wave (wn, wk) streams 16 rows of w2
-// over K slice wk (all S steps loaded at once when S > 0), then the WK
-// partial sums of each column group are reduced through LDS.
-template <int WN, int WK, int S>
-__global__ __launch_bounds__(64 * WN * WK) void ffn_mx_down(GroupedGemm g, int n_tiles) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wn = wave % WN, wk = wave / WN;
-  const int li = lane & 15, kb = lane >> 4;
-  TileMap tm;
-  tm.init(g.offsets, g.G, g.ident_rows, 16);
-  const int total = tm.total * n_tiles;
-  const int K = g.K;
-  const int Kw = K / WK, kbeg = wk * Kw;
-  for (int t = blockIdx.x; t < total; t += gridDim.x) {
-    const int id = xcd_remap(t, total);
-    const int n_tile = id / tm.total;
-    int grp, row0, nrows;
-    tm.find(id - n_tile * tm.total, grp, row0, nrows);
-    const int n0 = n_tile * 16 * WN + wn * 16;
-    const int r = row0 + min(li, nrows - 1);
-    const uint8_t* xa = static_cast<const uint8_t*>(g.A) + (size_t)r * K + kbeg + 16 * kb;
-    const uint8_t* xs = g.A_scales + (size_t)r * (K / 32) + kbeg / 32 + kb;
-    const uint8_t* wp = static_cast<const uint8_t*>(g.W) + (size_t)grp * g.w_gstride +
-                        (size_t)(n0 + li) * (K / 2) + (kbeg + 32 * kb) / 2;
-    const uint8_t* sp = g.W_scales + (size_t)grp * g.ws_gstride + (size_t)(n0 + li) * (K / 32) +
-                        kbeg / 32 + kb;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (S > 0) {
-      u32x4 wa[S > 0 ? S : 1];
-      uint32_t ws[S > 0 ? S : 1], xsc[S > 0 ? S : 1];
-      i32x8 xb[S > 0 ? S : 1];
-#pragma unroll
-      for (int u = 0; u < S; ++u) {
-        wa[u] = ld16_stream(wp + u * 64);
-        ws[u] = sp[u * 4];
-        xb[u] = ld32_fp8(xa + u * 128);
-        xsc[u] = xs[u * 4];
-      }
-#pragma unroll
-      for (int u = 0; u < S; ++u) acc = mfma_fp4_fp8(wa[u], xb[u], ws[u], xsc[u], acc);
+    for (int u = 0; u < U; ++u)
+      b.w[u][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)woff + u * 64, wso, 0);
+    const int sso = row0 * (K / 32) + st0 * 4;
+    if (U == 2) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(sr, (int)soff, sso, 0);
+      b.ws[0][j] = v.x;
+      b.ws[U - 1][j] = v.y;
     } else {
-      const int nsteps = Kw / 128;
-      for (int u = 0; u < nsteps; ++u)
-        acc = mfma_fp4_fp8(ld16_stream(wp + u * 64), ld32_fp8(xa + u * 128), sp[u * 4], xs[u * 4], acc);
+      b.ws[0][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, (int)soff, sso, 0);
     }
-    if (WK > 1) {
-      __shared__ f32x4 red[WK > 1 ? WK - 1 : 1][WN][64];
-      if (wk > 0) red[wk - 1][wn][lane] = acc;
-      __syncthreads();
-      if (wk == 0) {
+  }
 #pragma unroll
-        for (int w = 0; w < WK - 1; ++w) acc += red[w][wn][lane];
-      }
-      __syncthreads();
-      if (wk != 0) continue;
+  for (int u = 0; u < U; ++u) b.x[u] = ld32_fp8(t.xa + st0 * 128 + u * 128);
+  if (U == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(t.xs + st0 * 4);
+    b.xs[0] = v.x;
+    b.xs[U - 1] = v.y;
+  } else {
+    b.xs[0] = *reinterpret_cast<const uint32_t*>(t.xs + st0 * 4);
+  }
+}
+
+template <int U>
+__device__ __forceinline__ void mx_compute(const MxBatch<U>& b, f32x4* acc, int kb) {
+  const int sh = 8 * kb;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t xsc = (b.xs[u] >> sh) & 0xffu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[j] = mfma_fp4_fp8(b.w[u][j], b.x[u], (b.ws[u][j] >> sh) & 0xffu, xsc, acc[j]);
+  }
+}
+
+// D[n][m]: lane (li, kb) holds activation row li and, for weight group j,
+// output columns (group base) + 4*kb + i.
+template <bool SWIGLU>
+__device__ __forceinline__ void mx_store(const GroupedGemm& g, const MxTile& t, const f32x4* acc,
+                                         int li, int kb) {
+  if (SWIGLU) {
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = (acc[0][i] / (1.f + expf(-acc[0][i]))) * acc[2][i];
+      a[4 + i] = (acc[1][i] / (1.f + expf(-acc[1][i]))) * acc[3][i];
     }
-    if (li < nrows) {
-      const int nc = n0 + 4 * kb;
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    const int e = mx_exponent(amax);
+    const float inv = exp2_neg(e);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= e4m3_encode(a[i] * inv) << (8 * i);
+      hi |= e4m3_encode(a[4 + i] * inv) << (8 * i);
+    }
+    if (li < t.nrows) {
+      uint8_t* orow = static_cast<uint8_t*>(g.out) + (size_t)(t.row0 + li) * g.N;
+      *reinterpret_cast<uint32_t*>(orow + t.n0 + 4 * kb) = lo;
+      *reinterpret_cast<uint32_t*>(orow + t.n0 + 16 + 4 * kb) = hi;
+      if (kb == 0) g.out_scales[(size_t)(t.row0 + li) * (g.N / 32) + t.n0 / 32] = (uint8_t)(e + 127);
+    }
+  } else if (li < t.nrows) {
+    uint16_t* orow = static_cast<uint16_t*>(g.out) + (size_t)(t.row0 + li) * g.N + t.n0 + 4 * kb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
       u32x2 pk;
-      pk.x = pack_bf16x2(acc[0], acc[1]);
-      pk.y = pack_bf16x2(acc[2], acc[3]);
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(g.out) + (size_t)(row0 + li) * g.N + nc) = pk;
+      pk.x = pack_bf16x2(acc[j][0], acc[j][1]);
+      pk.y = pack_bf16x2(acc[j][2], acc[j][3]);
+      *reinterpret_cast<u32x2*>(orow + 16 * j) = pk;
     }
+  }
+}
+
+template <bool SWIGLU, int U>
+__global__ __launch_bounds__(256) void ffn_mx_stream(GroupedGemm g, int n_tiles) {
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, kb = lane >> 4;
+  // wave-major numbering: the first gridDim.x tiles go to wave 0 of every
+  // block, so however few tiles there are, they spread over all CUs
+  const int nw = gridDim.x * 4;
+  // (readfirstlane: these are wave-uniform, and the buffer loads need their
+  // scalar offsets in scalar registers)
+  const int gw = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) * gridDim.x + blockIdx.x);
+  TileMap tm;
+  tm.init(g.offsets, g.G, g.ident_rows, 16);
+  const int total = __builtin_amdgcn_readfirstlane(tm.total * n_tiles);
+  if (gw >= total) return;  // the kernel has no barriers
+  const int nb = g.K / 128 / U;
+  const uint32_t woff = (uint32_t)li * (uint32_t)(g.K / 2) + 16u * kb;
+  const uint32_t soff = (uint32_t)li * (uint32_t)(g.K / 32);
+  MxTile cur = mx_tile_at<SWIGLU>(g, tm, gw, li, kb);
+  MxBatch<U> b0, b1;
+  mx_load<SWIGLU, U>(b0, g, cur, 0, woff, soff);
+  for (int id = gw; id < total; id += nw) {
+    MxTile nxt = cur;
+    if (id + nw < total)
+      nxt = mx_tile_at<SWIGLU>(g, tm, id + nw, li, kb);
+    else
+      nxt.live = 0;  // the batch loaded past the last tile reads nothing
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < nb; b += 2) {
+      // batch b+1 -> b1 (the next tile's batch 0 after this tile's last)
+      mx_load<SWIGLU, U>(b1, g, b + 1 < nb ? cur : nxt, b + 1 < nb ? (b + 1) * U : 0, woff, soff);
+      __builtin_amdgcn_sched_barrier(0);
+      mx_compute<U>(b0, acc, kb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (b + 1 < nb) {
+        mx_load<SWIGLU, U>(b0, g, b + 2 < nb ? cur : nxt, b + 2 < nb ? (b + 2) * U : 0, woff,
+                           soff);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_compute<U>(b1, acc, kb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    mx_store<SWIGLU>(g, cur, acc, li, kb);
+    if (nb & 1) b0 = b1;  // an odd batch count left the next tile's first batch in b1
+    cur = nxt;
   }
 }
 
@@ -332,57 +347,37 @@ static inline long long mx_tiles_bound(const GroupedGemm& g, int n_tiles) {
   return ((long long)(g.total_rows + 15) / 16 + groups) * n_tiles;
 }
 
-template <int WK, int S>
-static void launch_mx_up(const GroupedGemm& g, hipStream_t s) {
-  const int nt = g.N / 32;
-  auto k = ffn_mx_up<WK, S>;
-  const int grid = resident_grid(reinterpret_cast<const void*>(k), 64 * WK, mx_tiles_bound(g, nt));
-  hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WK), 0, s, g, nt);
+// The buffer descriptors address one expert matrix with 32-bit offsets.
+static inline bool mx_matrix_fits(const GroupedGemm& g, bool swiglu) {
+  const long long rows = swiglu ? 2ll * g.up_off : (long long)g.N;
+  return rows * (g.K / 2) < (1ll << 31);
 }
 
-// K = H: 128-wide steps split over WK waves, S steps each (all in flight).
+template <bool SWIGLU, int U>
+static void launch_mx_stream(const GroupedGemm& g, hipStream_t s) {
+  const int nt = g.N / (SWIGLU ? 32 : 64);
+  auto k = ffn_mx_stream<SWIGLU, U>;
+  const int grid = resident_grid(reinterpret_cast<const void*>(k), 256, (mx_tiles_bound(g, nt) + 3) / 4);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, g, nt);
+}
+
+// K = H (a multiple of 256): batches of 2 K-steps.
 int launch_ffn_up_w4a8(const GroupedGemm& g, hipStream_t s) {
-  const int steps = g.K / 128;
-  if (steps == 32)
-    launch_mx_up<8, 4>(g, s);
-  else if (steps == 16)
-    launch_mx_up<4, 4>(g, s);
-  else if (steps == 8)
-    launch_mx_up<2, 4>(g, s);
-  else if (steps == 4)
-    launch_mx_up<1, 4>(g, s);
-  else if (steps == 2)
-    launch_mx_up<1, 2>(g, s);
-  else if (steps % 4 == 0)
-    launch_mx_up<4, 0>(g, s);
+  if (!mx_matrix_fits(g, true)) return -3;  // MOE_ERR_UNSUPPORTED
+  if ((g.K / 128) % 2 == 0)
+    launch_mx_stream<true, 2>(g, s);
   else
-    launch_mx_up<1, 0>(g, s);
+    launch_mx_stream<true, 1>(g, s);
   return launch_status();
 }
 
-template <int WN, int WK, int S>
-static void launch_mx_down(const GroupedGemm& g, hipStream_t s) {
-  const int nt = g.N / (16 * WN);
-  auto k = ffn_mx_down<WN, WK, S>;
-  const int grid = resident_grid(reinterpret_cast<const void*>(k), 64 * WN * WK, mx_tiles_bound(g, nt));
-  hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WN * WK), 0, s, g, nt);
-}
-
-// K = I: same idea; N = H is a multiple of 64.
+// K = I (a multiple of 128); N = H (a multiple of 64).
 int launch_ffn_down_w4a8(const GroupedGemm& g, hipStream_t s) {
-  const int steps = g.K / 128;
-  if (steps == 12)
-    launch_mx_down<4, 1, 12>(g, s);
-  else if (steps == 8)
-    launch_mx_down<2, 2, 4>(g, s);
-  else if (steps == 4)
-    launch_mx_down<4, 1, 4>(g, s);
-  else if (steps == 2)
-    launch_mx_down<4, 1, 2>(g, s);
-  else if (steps == 1)
-    launch_mx_down<4, 1, 1>(g, s);
+  if (!mx_matrix_fits(g, false)) return -3;  // MOE_ERR_UNSUPPORTED
+  if ((g.K / 128) % 2 == 0)
+    launch_mx_stream<false, 2>(g, s);
   else
-    launch_mx_down<4, 1, 0>(g, s);
+    launch_mx_stream<false, 1>(g, s);
   return launch_status();
 }
 

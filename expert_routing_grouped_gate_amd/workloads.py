@@ -36,7 +36,7 @@ import torch
 
 # tensor tags used in seed derivation
 _TAG_X, _TAG_ROUTER, _TAG_BIAS, _TAG_W13, _TAG_W2, _TAG_SHARED = 1, 2, 3, 4, 5, 6
-_TAG_MX_W13, _TAG_MX_W2 = 7, 8
+_TAG_MX_W13, _TAG_MX_W2, _TAG_MX_SHARED = 7, 8, 9
 
 
 @dataclass(frozen=True)
@@ -184,6 +184,17 @@ def draw_expert_mx(cfg: LayerConfig, e: int):
     return c13, s13, c2, s2
 
 
+def draw_shared_mx(cfg: LayerConfig):
+    """The shared expert in W4A8: (w13_codes [2*shared_I, H/2], w13_scales,
+    w2_codes [H, shared_I/2], w2_scales), same distributions as the routed
+    experts."""
+    assert cfg.shared_I > 0
+    Is = cfg.shared_I
+    c13, s13 = _mx_block(2 * Is, cfg.H, cfg.family_seed, _TAG_MX_SHARED, 0, Is, cfg.H)
+    c2, s2 = _mx_block(cfg.H, Is, cfg.family_seed, _TAG_MX_SHARED, 1, Is, cfg.H)
+    return c13, s13, c2, s2
+
+
 def describe(cfg: LayerConfig) -> dict:
     d = dataclasses.asdict(cfg)
     d["R"] = cfg.R
@@ -195,7 +206,8 @@ def draw_layer(cfg: LayerConfig, progress=None) -> dict:
 
     bf16: w13 [E, 2I, H], w2 [E, H, I] (+ shared_w13, shared_w2).
     w4a8: w13 codes [E, 2I, H/2], w13_scales [E, 2I, H/32], w2 codes
-    [E, H, I/2], w2_scales [E, H, I/32]."""
+    [E, H, I/2], w2_scales [E, H, I/32] (+ the shared expert's codes and
+    scales)."""
     t = {"x": draw_x(cfg), "wr": draw_router(cfg), "bias": draw_bias(cfg)}
     E = cfg.E
     if cfg.fmt == "bf16":
@@ -218,4 +230,7 @@ def draw_layer(cfg: LayerConfig, progress=None) -> dict:
             if progress is not None and (e % 32 == 31 or e == E - 1):
                 progress(f"{cfg.name}: drew experts 0..{e}")
         t["w13"], t["w13_scales"], t["w2"], t["w2_scales"] = c13, s13, c2, s2
+        if cfg.shared_I:
+            (t["shared_w13"], t["shared_w13_scales"], t["shared_w2"],
+             t["shared_w2_scales"]) = draw_shared_mx(cfg)
     return t

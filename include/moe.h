@@ -26,7 +26,8 @@
  *     (an expert id outside [0, E)) are reported in a device status word.
  *   - T == 0 (no tokens) is valid and enqueues nothing.
  *   - Limits: 1 <= k <= min(E, 32); 1 <= E <= 256; H % 256 == 0;
- *     I % 128 == 0; T * k < 2^31.
+ *     I % 128 == 0; T * k < 2^31; W4A8: max(I, shared_I) * H < 2^31 (one
+ *     expert's E2M1 matrix is addressed with 32-bit offsets).
  */
 #ifndef MOE_H
 #define MOE_H

@@ -23,7 +23,8 @@ class Layer:
         self.weights = B.ExpertWeights(
             H=cfg.H, I=cfg.I, E=cfg.E, fmt=fmt, w13=d["w13"], w2=d["w2"],
             w13_scales=d.get("w13_scales"), w2_scales=d.get("w2_scales"),
-            shared_I=cfg.shared_I, shared_w13=d.get("shared_w13"), shared_w2=d.get("shared_w2"))
+            shared_I=cfg.shared_I, shared_w13=d.get("shared_w13"), shared_w2=d.get("shared_w2"),
+            shared_w13_scales=d.get("shared_w13_scales"), shared_w2_scales=d.get("shared_w2_scales"))
         self.mode = B.GATE_SIGMOID if cfg.gate == "sigmoid" else B.GATE_SOFTMAX
 
     def layer(self):
@@ -53,6 +54,10 @@ class Layer:
         c = self.cpu
         if not self.cfg.shared_I:
             return None
+        if self.cfg.fmt == "w4a8":
+            return (mx.mxfp4_dequant(c["shared_w13"].numpy(), c["shared_w13_scales"].numpy(), self.cfg.H),
+                    mx.mxfp4_dequant(c["shared_w2"].numpy(), c["shared_w2_scales"].numpy(),
+                                     self.cfg.shared_I))
         return (c["shared_w13"].to(torch.float64).numpy(), c["shared_w2"].to(torch.float64).numpy())
 
     def oracle(self, logits=None, tokens=None):
@@ -65,7 +70,8 @@ class Layer:
 
 _CACHE = {}
 _WCACHE = {}
-_WKEYS = ("w13", "w2", "w13_scales", "w2_scales", "shared_w13", "shared_w2")
+_WKEYS = ("w13", "w2", "w13_scales", "w2_scales", "shared_w13", "shared_w2", "shared_w13_scales",
+          "shared_w2_scales")
 
 
 def _to_dev(d):

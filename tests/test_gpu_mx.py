@@ -20,6 +20,13 @@ SMALL = {
     "mx_mid": CFG["qwen3_decode_w4a8"].with_(name="mx_mid", T=37, H=1024, E=16, k=4, I=256,
                                              family_seed=1106, x_seed=22),
     "mx_decode_shape": CFG["qwen3_decode_w4a8"].with_(name="mx_decode_shape", T=5, x_seed=23),
+    # more tiles than the grid has waves: every wave streams several tiles
+    # back to back (its next tile's first loads overlap the current tile)
+    "mx_many_tiles": CFG["qwen3_decode_w4a8"].with_(name="mx_many_tiles", T=1024, H=256, E=8, k=4,
+                                                    I=512, family_seed=1107, x_seed=24),
+    # Hy3-style gate with an always-on W4A8 shared expert
+    "mx_shared": CFG["hy3"].with_(name="mx_shared", T=40, H=512, E=16, k=4, I=256, shared_I=384,
+                                  fmt="w4a8", family_seed=1108, x_seed=25),
 }
 
 
@@ -50,14 +57,20 @@ def test_mx_quantize_bit_exact(rows, cols, scale):
 def _quant_codes_close(gpu_codes, gpu_scales, ref_vals, what):
     """The GPU quantises fp32 values, the oracle the fp64 ones; allow a code
     to differ by one E4M3 step on a small fraction of elements (values that
-    sit next to a rounding boundary)."""
+    sit next to a rounding boundary).  The value quantised is SiLU(g) * u of
+    two fp32 dot products over K, whose rounding error is absolute: relative
+    to the largest value of its 32-block, about 2^-14 covers it, so elements
+    that cancel to almost zero are held to that instead of one E4M3 step."""
     gv = mx.mxfp8_dequant(gpu_codes, gpu_scales)
     rc, rs = mx.mxfp8_quantize(ref_vals)
     rv = mx.mxfp8_dequant(rc, rs)
     same = gv == rv
     assert same.mean() > 0.995, f"{what}: only {same.mean():.4f} of codes equal"
     d = np.abs(gv - rv)
-    assert np.all(d <= np.abs(rv) * 0.126 + np.repeat(mx.e8m0_decode(rs), 32, -1) * 2.0 ** -9 * 1.01), what
+    rows, cols = rv.shape
+    amax = np.repeat(np.abs(ref_vals).reshape(rows, cols // 32, 32).max(-1), 32, -1)
+    step = np.abs(rv) * 0.126 + np.repeat(mx.e8m0_decode(rs), 32, -1) * 2.0 ** -9 * 1.01
+    assert np.all(d <= np.maximum(step, amax * 2.0 ** -14)), what
 
 
 @pytest.mark.parametrize("name", list(SMALL))

@@ -37,3 +37,12 @@ def test_mx_weights_shapes_and_codes():
     assert c2.shape == (256, 64) and s2.shape == (256, 4)
     assert set(torch.unique(s13).tolist()) <= {119, 120, 121}
     assert c13.dtype == torch.uint8
+
+
+def test_mx_shared_expert_drawn_with_layer():
+    c = W.CONFIGS["qwen3_decode_w4a8"].with_(T=2, H=256, E=4, I=128, shared_I=128)
+    t = W.draw_layer(c)
+    assert t["shared_w13"].shape == (256, 128) and t["shared_w13_scales"].shape == (256, 8)
+    assert t["shared_w2"].shape == (256, 64) and t["shared_w2_scales"].shape == (256, 4)
+    c13, _, _, _ = W.draw_expert_mx(c, 0)
+    assert not torch.equal(t["shared_w13"], c13)   # its own stream, not expert 0's
