@@ -65,6 +65,8 @@ SIGNATURES = {
     "moe_route_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route": (_I, [_vp, _I, _I, _I, _vp, _vp, _vp, _vp, _vp, _vp, _SZ, _vp]),
     "moe_mx_quantize": (_I, [_vp, _I, _I, _vp, _vp, _vp]),
+    "moe_mx_packed_scales_bytes": (_SZ, [_I, _I]),
+    "moe_mx_pack_weight": (_I, [_vp, _vp, _I, _I, _I, _vp, _vp, _vp]),
     "moe_grouped_ffn_up": (_I, [_P(MoeFfnWeights), _vp, _vp, _I, _I, _vp, _vp, _vp, _vp, _vp]),
     "moe_grouped_ffn_down": (_I, [_P(MoeFfnWeights), _vp, _vp, _I, _I, _vp, _vp, _vp]),
     "moe_shared_ffn": (_I, [_P(MoeFfnWeights), _vp, _vp, _I, _vp, _vp, _vp, _vp]),
@@ -183,9 +185,31 @@ def mx_quantize(x: torch.Tensor):
     return codes, scales
 
 
+def mx_pack_weight(codes: torch.Tensor, scales: torch.Tensor):
+    """Packed layout of MX weights (moe_mx_pack_weight): codes [G, R, K/2] or
+    [R, K/2] and scales [G, R, K/32] -> (packed codes, same shape; packed
+    scales, uint8 [G, moe_mx_packed_scales_bytes(R, K)] or [bytes])."""
+    _dev(codes, scales)
+    flat = codes.dim() == 2
+    c3 = codes.unsqueeze(0) if flat else codes
+    s3 = scales.unsqueeze(0) if flat else scales
+    G, R, K2 = c3.shape
+    K = 2 * K2
+    assert c3.dtype == torch.uint8 and s3.dtype == torch.uint8 and s3.shape == (G, R, K // 32)
+    nbytes = load().moe_mx_packed_scales_bytes(R, K)
+    pc = torch.empty_like(c3)
+    ps = torch.empty((G, nbytes), dtype=torch.uint8, device=c3.device)
+    _check("moe_mx_pack_weight", load().moe_mx_pack_weight(
+        _ptr(c3.contiguous()), _ptr(s3.contiguous()), G, R, K, _ptr(pc), _ptr(ps), _stream()))
+    return (pc[0], ps[0]) if flat else (pc, ps)
+
+
 @dataclass
 class ExpertWeights:
-    """Device weights of one MoE layer (see MoeFfnWeights in include/moe.h)."""
+    """Device weights of one MoE layer (see MoeFfnWeights in include/moe.h).
+    W4A8 weights are given in the plain layout (codes [.., R, K/2], scales
+    [.., R, K/32]) and packed once here; the packed copies are what the
+    library reads."""
     H: int
     I: int
     E: int
@@ -200,13 +224,26 @@ class ExpertWeights:
     shared_w13_scales: Optional[torch.Tensor] = None
     shared_w2_scales: Optional[torch.Tensor] = None
 
+    def __post_init__(self):
+        self._lib_view = {k: getattr(self, k) for k in _WFIELDS}
+        if self.fmt == FMT_W4A8:
+            for codes, scales in (("w13", "w13_scales"), ("w2", "w2_scales"),
+                                  ("shared_w13", "shared_w13_scales"), ("shared_w2", "shared_w2_scales")):
+                c, sc = getattr(self, codes), getattr(self, scales)
+                if c is not None:
+                    self._lib_view[codes], self._lib_view[scales] = mx_pack_weight(c, sc)
+
     def c_struct(self) -> MoeFfnWeights:
-        _dev(self.w13, self.w2, self.w13_scales, self.w2_scales, self.shared_w13, self.shared_w2,
-             self.shared_w13_scales, self.shared_w2_scales)
-        return MoeFfnWeights(self.H, self.I, self.E, self.fmt, _ptr(self.w13), _ptr(self.w13_scales),
-                             _ptr(self.w2), _ptr(self.w2_scales), self.shared_I, _ptr(self.shared_w13),
-                             _ptr(self.shared_w13_scales), _ptr(self.shared_w2),
-                             _ptr(self.shared_w2_scales))
+        v = self._lib_view
+        _dev(*(v[k] for k in _WFIELDS))
+        return MoeFfnWeights(self.H, self.I, self.E, self.fmt, _ptr(v["w13"]), _ptr(v["w13_scales"]),
+                             _ptr(v["w2"]), _ptr(v["w2_scales"]), self.shared_I, _ptr(v["shared_w13"]),
+                             _ptr(v["shared_w13_scales"]), _ptr(v["shared_w2"]),
+                             _ptr(v["shared_w2_scales"]))
+
+
+_WFIELDS = ("w13", "w13_scales", "w2", "w2_scales", "shared_w13", "shared_w13_scales", "shared_w2",
+            "shared_w2_scales")
 
 
 def _act_tensors(rows: int, I: int, fmt: int, device):

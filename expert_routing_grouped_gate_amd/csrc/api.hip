@@ -200,6 +200,22 @@ int moe_mx_quantize(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8
   return moe::launch_mx_quantize(x, rows, cols, codes, scales, as_stream(stream));
 }
 
+size_t moe_mx_packed_scales_bytes(int rows, int K) {
+  if (rows <= 0 || K <= 0 || rows % 16 != 0 || K % 128 != 0) return 0;
+  return moe::mx_packed_scales_bytes(rows, K);
+}
+
+int moe_mx_pack_weight(const uint8_t* codes, const uint8_t* scales, int G, int rows, int K,
+                       uint8_t* packed_codes, uint8_t* packed_scales, void* stream) {
+  int st;
+  if (G < 0 || rows <= 0 || K <= 0) return MOE_ERR_SHAPE;
+  if (rows % 16 != 0 || K % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (G == 0) return MOE_OK;
+  if ((st = check_ptrs({codes, scales, packed_codes, packed_scales}))) return st;
+  return moe::launch_mx_pack(codes, scales, G, rows, K, packed_codes, packed_scales,
+                             as_stream(stream));
+}
+
 int moe_grouped_ffn_up(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales, int T,
                        int k, const int32_t* sorted_pair, const int32_t* offsets, void* act,
                        uint8_t* act_scales, void* stream) {
@@ -224,7 +240,7 @@ int moe_grouped_ffn_up(const MoeFfnWeights* w, const void* x, const uint8_t* x_s
   g.out_scales = act_scales;
   if (mx) {
     g.w_gstride = (long long)w->I * w->H;  // bytes: 2I rows of H/2
-    g.ws_gstride = 2ll * w->I * (w->H / 32);
+    g.ws_gstride = (long long)moe::mx_packed_scales_bytes(2 * w->I, w->H);
     return moe::launch_ffn_up_w4a8(g, as_stream(stream));
   }
   g.w_gstride = 2ll * w->I * w->H;
@@ -253,7 +269,7 @@ int moe_grouped_ffn_down(const MoeFfnWeights* w, const void* act, const uint8_t*
   g.out = y;
   if (mx) {
     g.w_gstride = (long long)w->H * (w->I / 2);
-    g.ws_gstride = (long long)w->H * (w->I / 32);
+    g.ws_gstride = (long long)moe::mx_packed_scales_bytes(w->H, w->I);
     return moe::launch_ffn_down_w4a8(g, as_stream(stream));
   }
   g.w_gstride = (long long)w->H * w->I;

@@ -58,6 +58,12 @@ int launch_ffn_down_w4a8(const GroupedGemm& g, hipStream_t s);
 int launch_mx_quantize(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
                        hipStream_t s);
 
+// Packed W4A8 weights (layout in mx.hip): scale bytes of one matrix, and the
+// pack of G matrices of R x K.
+size_t mx_packed_scales_bytes(int rows, int K);
+int launch_mx_pack(const uint8_t* codes, const uint8_t* scales, int G, int R, int K,
+                   uint8_t* packed_codes, uint8_t* packed_scales, hipStream_t s);
+
 int launch_combine(const uint16_t* y, const int32_t* pair_pos, const float* w,
                    const uint16_t* shared_y, int T, int k, int H, uint16_t* out, hipStream_t s);
 

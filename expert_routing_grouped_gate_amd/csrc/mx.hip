@@ -111,6 +111,68 @@ int launch_mx_quantize(const uint16_t* x, int rows, int cols, uint8_t* codes, ui
   return launch_status();
 }
 
+// ------------------------------------------------------- weight pack -----
+// Packed W4A8 weight layout, per matrix of R rows (R % 16 == 0) and K
+// reduction columns (K % 128 == 0), ns = K/128 steps, nq = ceil(ns/4):
+//   codes : block (q, s) at byte (q*ns + s)*1024 (q = group of 16 rows,
+//           s = K-step); its lane l = 16*kb + i holds the 16 bytes
+//           [64s + 16kb, +16) of row 16q + i, i.e. E2M1 k = 128s + 32kb ..
+//           +31: exactly the A operand of lane l for step s.
+//   scales: block (q, c) at byte (q*nq + c)*256; lane l = 16*kb + i holds a
+//           dword whose byte u is the E8M0 scale of row 16q + i, 32-block
+//           4(4c + u) + kb (steps 4c .. 4c+3; zero past the last step).
+// Codes keep their size; scales grow only when ns % 4 != 0.
+size_t mx_packed_scales_bytes(int rows, int K) {
+  const int ns = K / 128, nq = (ns + 3) / 4;
+  return (size_t)(rows / 16) * (size_t)nq * 256u;
+}
+
+__global__ __launch_bounds__(256) void mx_pack_codes(const uint8_t* __restrict__ codes, long long n,
+                                                     int R, int K, uint8_t* __restrict__ pc) {
+  const int ns = K / 128;
+  for (long long c = (long long)blockIdx.x * 256 + threadIdx.x; c < n;
+       c += (long long)gridDim.x * 256) {
+    // c = ((g*(R/16) + q)*ns + s)*64 + l: the 16-byte chunk c of the packed matrix
+    const int l = (int)(c & 63);
+    const long long blk = c >> 6;
+    const int s = (int)(blk % ns);
+    const long long gq = blk / ns;  // g*(R/16) + q
+    const long long row = gq * 16 + (l & 15);  // global row g*R + 16q + i
+    const u32x4 v = ld16(codes + row * (K / 2) + s * 64 + 16 * (l >> 4));
+    *reinterpret_cast<u32x4*>(pc + c * 16) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void mx_pack_scales(const uint8_t* __restrict__ scales, long long n,
+                                                      int R, int K, uint8_t* __restrict__ ps) {
+  const int ns = K / 128, nq = (ns + 3) / 4;
+  for (long long d = (long long)blockIdx.x * 256 + threadIdx.x; d < n;
+       d += (long long)gridDim.x * 256) {
+    // d = ((g*(R/16) + q)*nq + c)*64 + l: the dword d of the packed scales
+    const int l = (int)(d & 63);
+    const long long blk = d >> 6;
+    const int c = (int)(blk % nq);
+    const long long row = (blk / nq) * 16 + (l & 15);
+    uint32_t w = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int st = 4 * c + u;
+      if (st < ns) w |= (uint32_t)scales[row * (K / 32) + 4 * st + (l >> 4)] << (8 * u);
+    }
+    *reinterpret_cast<uint32_t*>(ps + d * 4) = w;
+  }
+}
+
+int launch_mx_pack(const uint8_t* codes, const uint8_t* scales, int G, int R, int K,
+                   uint8_t* pc, uint8_t* ps, hipStream_t s) {
+  const long long nc = (long long)G * R * (K / 32);                        // 16-byte chunks
+  const long long nd = (long long)G * (long long)(mx_packed_scales_bytes(R, K) / 4);  // dwords
+  const int grid = 2048;
+  hipLaunchKernelGGL(mx_pack_codes, dim3(grid), dim3(256), 0, s, codes, nc, R, K, pc);
+  hipLaunchKernelGGL(mx_pack_scales, dim3(grid), dim3(256), 0, s, scales, nd, R, K, ps);
+  return launch_status();
+}
+
 // -------------------------------------------------------- scaled MFMA -----
 __device__ __forceinline__ f32x4 mfma_fp4_fp8(u32x4 a_fp4, i32x8 b_fp8, uint32_t sa, uint32_t sb,
                                               f32x4 c) {
@@ -172,10 +234,11 @@ __device__ __forceinline__ MxTile mx_tile_at(const GroupedGemm& g, const TileMap
 
 template <int U>
 struct MxBatch {
-  u32x4 w[U][4];      // E2M1 weights, 32 k per lane
-  i32x8 x[U];         // E4M3 activations, 32 k per lane
-  uint32_t ws[U][4];  // 4 scale bytes per word; this lane's is byte kb
-  uint32_t xs[U];
+  u32x4 w[U][4];   // E2M1 weights, 32 k per lane
+  i32x8 x[U];      // E4M3 activations, 32 k per lane
+  uint32_t ws[4];  // packed weight scales: byte (step & 3) of the step's quad
+  uint32_t xs[U];  // activation scale words; this lane's byte is kb
+  int sh;          // 8 * (first step & 3): bit offset of the first step's byte
 };
 
 // First row of weight group j (uniform); the lane adds li.
@@ -192,39 +255,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* p, uint32_
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// Batch of U K-steps (128 each) starting at step st0 of tile t.  Weights and
-// their scales are read through buffer descriptors over the expert's matrix:
-// the lane offset (woff = li*K/2 + 16*kb, soff = li*K/32) is the same for
-// every tile and every step, the row group and step go into the scalar
-// offset, so the weight stream needs no per-tile vector address registers.
+// Batch of U K-steps (128 each) starting at step st0 of tile t.  The weights
+// are in the packed layout (moe_mx_pack_weight): the 16 rows of group j for
+// one step are one contiguous 1 KB block in lane order, their scales for 4
+// steps one 256-byte block (a dword per lane).  Both are read through buffer
+// descriptors over the expert's matrix: the lane offset is fixed, the block
+// index goes into the scalar offset, so each load instruction reads whole
+// cache lines and the stream needs no per-tile vector address registers.
 template <bool SWIGLU, int U>
 __device__ __forceinline__ void mx_load(MxBatch<U>& b, const GroupedGemm& g, const MxTile& t,
-                                        int st0, uint32_t woff, uint32_t soff) {
-  const int K = g.K;
+                                        int st0, int lane) {
+  const int ns = g.K / 128, nq = (ns + 3) / 4;  // K-steps, scale quads per row group
   // a dead tile gets empty descriptors: its loads return zeros without a
   // memory access
   const uint32_t wrows = SWIGLU ? 2u * (uint32_t)g.up_off : (uint32_t)g.N;  // rows of one matrix
   const __amdgpu_buffer_rsrc_t wr =
       mx_rsrc(static_cast<const uint8_t*>(g.W) + (size_t)t.grp * g.w_gstride,
-              t.live ? wrows * (uint32_t)(K / 2) : 0u);
+              t.live ? wrows * (uint32_t)(g.K / 2) : 0u);
   const __amdgpu_buffer_rsrc_t sr = mx_rsrc(g.W_scales + (size_t)t.grp * g.ws_gstride,
-                                            t.live ? wrows * (uint32_t)(K / 32) : 0u);
+                                            t.live ? wrows / 16u * (uint32_t)nq * 256u : 0u);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row0 = mx_wrow0<SWIGLU>(g, t.n0, j);
-    const int wso = row0 * (K / 2) + st0 * 64;
+    const int q = mx_wrow0<SWIGLU>(g, t.n0, j) / 16;
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      b.w[u][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)woff + u * 64, wso, 0);
-    const int sso = row0 * (K / 32) + st0 * 4;
-    if (U == 2) {
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(sr, (int)soff, sso, 0);
-      b.ws[0][j] = v.x;
-      b.ws[U - 1][j] = v.y;
-    } else {
-      b.ws[0][j] = __builtin_amdgcn_raw_buffer_load_b32(sr, (int)soff, sso, 0);
-    }
+      b.w[u][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, lane * 16, (q * ns + st0 + u) * 1024, 0);
+    // U <= 2 and st0 % U == 0: the batch's steps share one quad
+    b.ws[j] = __builtin_amdgcn_raw_buffer_load_b32(sr, lane * 4, (q * nq + st0 / 4) * 256, 0);
   }
+  b.sh = 8 * (st0 & 3);
 #pragma unroll
   for (int u = 0; u < U; ++u) b.x[u] = ld32_fp8(t.xa + st0 * 128 + u * 128);
   if (U == 2) {
@@ -244,7 +303,7 @@ __device__ __forceinline__ void mx_compute(const MxBatch<U>& b, f32x4* acc, int 
     const uint32_t xsc = (b.xs[u] >> sh) & 0xffu;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[j] = mfma_fp4_fp8(b.w[u][j], b.x[u], (b.ws[u][j] >> sh) & 0xffu, xsc, acc[j]);
+      acc[j] = mfma_fp4_fp8(b.w[u][j], b.x[u], (b.ws[j] >> (b.sh + 8 * u)) & 0xffu, xsc, acc[j]);
   }
 }
 
@@ -306,11 +365,9 @@ __global__ __launch_bounds__(256) void ffn_mx_stream(GroupedGemm g, int n_tiles)
   const int total = __builtin_amdgcn_readfirstlane(tm.total * n_tiles);
   if (gw >= total) return;  // the kernel has no barriers
   const int nb = g.K / 128 / U;
-  const uint32_t woff = (uint32_t)li * (uint32_t)(g.K / 2) + 16u * kb;
-  const uint32_t soff = (uint32_t)li * (uint32_t)(g.K / 32);
   MxTile cur = mx_tile_at<SWIGLU>(g, tm, gw, li, kb);
   MxBatch<U> b0, b1;
-  mx_load<SWIGLU, U>(b0, g, cur, 0, woff, soff);
+  mx_load<SWIGLU, U>(b0, g, cur, 0, lane);
   for (int id = gw; id < total; id += nw) {
     MxTile nxt = cur;
     if (id + nw < total)
@@ -322,13 +379,12 @@ __global__ __launch_bounds__(256) void ffn_mx_stream(GroupedGemm g, int n_tiles)
     for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int b = 0; b < nb; b += 2) {
       // batch b+1 -> b1 (the next tile's batch 0 after this tile's last)
-      mx_load<SWIGLU, U>(b1, g, b + 1 < nb ? cur : nxt, b + 1 < nb ? (b + 1) * U : 0, woff, soff);
+      mx_load<SWIGLU, U>(b1, g, b + 1 < nb ? cur : nxt, b + 1 < nb ? (b + 1) * U : 0, lane);
       __builtin_amdgcn_sched_barrier(0);
       mx_compute<U>(b0, acc, kb);
       __builtin_amdgcn_sched_barrier(0);
       if (b + 1 < nb) {
-        mx_load<SWIGLU, U>(b0, g, b + 2 < nb ? cur : nxt, b + 2 < nb ? (b + 2) * U : 0, woff,
-                           soff);
+        mx_load<SWIGLU, U>(b0, g, b + 2 < nb ? cur : nxt, b + 2 < nb ? (b + 2) * U : 0, lane);
         __builtin_amdgcn_sched_barrier(0);
         mx_compute<U>(b1, acc, kb);
         __builtin_amdgcn_sched_barrier(0);

@@ -139,6 +139,26 @@ int moe_route(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
 int moe_mx_quantize(const uint16_t* x, int rows, int cols, uint8_t* codes,
                     uint8_t* scales, void* stream);
 
+/* ------------------------------------------------ W4A8 weight layout -----
+ * One-time re-layout of MX weights at load time ([Hy3] section 6.2, "GMM
+ * and weight layout": the expert weight layout is settled when the weights
+ * are loaded, so the decode step never re-arranges them).  Input: G matrices
+ * of rows x K (rows % 16 == 0, K % 128 == 0), E2M1 codes [G, rows, K/2] (low
+ * nibble = even k) and E8M0 scales [G, rows, K/32].  Output, per matrix
+ * (ns = K/128, nq = ceil(ns/4)):
+ *   packed_codes  (rows*K/2 bytes): 1 KB block (q, s) at (q*ns + s)*1024,
+ *                 q = group of 16 rows, s = 128-wide K step; its 16-byte
+ *                 lane l = 16*b + i is bytes [64s + 16b, +16) of row 16q + i.
+ *   packed_scales (moe_mx_packed_scales_bytes(rows, K) bytes): 256-byte
+ *                 block (q, c) at (q*nq + c)*256; its dword lane l = 16*b + i
+ *                 has in byte u the scale of row 16q + i, 32-block
+ *                 4*(4c + u) + b (zero beyond the last step).
+ * The inputs are only read; outputs are caller-owned device memory.
+ * moe_mx_packed_scales_bytes returns 0 for unsupported shapes. */
+size_t moe_mx_packed_scales_bytes(int rows, int K);
+int moe_mx_pack_weight(const uint8_t* codes, const uint8_t* scales, int G, int rows, int K,
+                       uint8_t* packed_codes, uint8_t* packed_scales, void* stream);
+
 /* ---------------------------------------------------------- S5, S6 -----
  * Expert weights.  [out, in] layout, K-contiguous ([Hy3] section 6.2 keeps
  * the checkpoint layout and multiplies through a transposed view).
@@ -146,12 +166,15 @@ int moe_mx_quantize(const uint16_t* x, int rows, int cols, uint8_t* codes,
  *         ([Qwen3] compute decomposition: gate and up concatenated; the
  *         SwiGLU takes SiLU of the first half times the second half)
  *         w2  [E, H, I]
- *   W4A8: w13 E2M1 codes [E, 2I, H/2] (low nibble = even k),
- *         w13_scales E8M0 [E, 2I, H/32]; w2 codes [E, H, I/2],
- *         w2_scales [E, H, I/32].
+ *   W4A8: the matrices above as E2M1 codes (low nibble = even k) with one
+ *         E8M0 scale per 32 consecutive k, in the packed layout written by
+ *         moe_mx_pack_weight: w13 = packed codes of [E, 2I, H/2] (same size),
+ *         w13_scales = E x moe_mx_packed_scales_bytes(2I, H) bytes; w2 =
+ *         packed codes of [E, H, I/2], w2_scales = E x
+ *         moe_mx_packed_scales_bytes(H, I) bytes.
  *   The optional shared expert ([Hy3] section 1.1: one per MoE layer, added
  *   to every token) uses the same format with intermediate shared_I
- *   (shared_I == 0: none). */
+ *   (shared_I == 0: none; W4A8: packed as one matrix each). */
 typedef struct {
   int H, I, E;
   int fmt; /* moe_format */

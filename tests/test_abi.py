@@ -122,3 +122,24 @@ def test_layer_forward_checks(lib):
     d2 = B.MoeLayerDesc(512, 8, 2, 0, 1.0, 1e-20, FAKE, None, w)
     assert f(ctypes.byref(d2), FAKE, 4, FAKE, ctypes.byref(b), None) == SHAPE  # H mismatch
     assert lib.moe_layer_workspace_size(ctypes.byref(d), 16) == 0
+
+
+def test_mx_pack_checks_and_sizes(lib):
+    size = lib.moe_mx_packed_scales_bytes
+    assert size(3072, 4096) == 3072 * 4096 // 32          # 8 steps per quad boundary: no padding
+    assert size(4096, 1536) == 4096 * 1536 // 32
+    assert size(16, 384) == 256                            # 3 steps padded to one quad
+    assert size(15, 4096) == 0 and size(16, 100) == 0
+    f = lib.moe_mx_pack_weight
+    assert f(FAKE, FAKE, 2, 15, 256, FAKE, FAKE, None) == UNSUP
+    assert f(FAKE, FAKE, 2, 16, 200, FAKE, FAKE, None) == UNSUP
+    assert f(FAKE, None, 2, 16, 256, FAKE, FAKE, None) == NULL
+    assert f(FAKE, FAKE, 2, 16, 256, MIS, FAKE, None) == ALIGN
+    assert f(FAKE, FAKE, -1, 16, 256, FAKE, FAKE, None) == SHAPE
+    assert f(None, None, 0, 16, 256, None, None, None) == OK   # nothing to pack
+
+
+def test_w4a8_matrix_size_limit(lib):
+    # one expert's E2M1 matrix must be addressable with 32-bit offsets
+    big = B.MoeFfnWeights(1 << 16, 1 << 15, 8, B.FMT_W4A8, FAKE, FAKE, FAKE, FAKE, 0, None, None, None, None)
+    assert lib.moe_grouped_ffn_up(ctypes.byref(big), FAKE, FAKE, 4, 2, FAKE, FAKE, FAKE, FAKE, None) == UNSUP

@@ -73,6 +73,31 @@ def _quant_codes_close(gpu_codes, gpu_scales, ref_vals, what):
     assert np.all(d <= np.maximum(step, amax * 2.0 ** -14)), what
 
 
+def _np_pack(codes, scales):
+    """The packed W4A8 layout as include/moe.h defines it, by reshapes."""
+    G, R, K2 = codes.shape
+    K = 2 * K2
+    ns, q16 = K // 128, R // 16
+    nq = (ns + 3) // 4
+    pc = codes.reshape(G, q16, 16, ns, 4, 16).transpose(0, 1, 3, 4, 2, 5)   # g q s b i byte
+    sc = np.zeros((G, q16, 16, nq * 4, 4), np.uint8)                       # g q i step b
+    sc[:, :, :, :ns] = scales.reshape(G, q16, 16, ns, 4)
+    ps = sc.reshape(G, q16, 16, nq, 4, 4).transpose(0, 1, 3, 5, 2, 4)       # g q c b i u
+    return pc.reshape(G, R, K2), ps.reshape(G, -1)
+
+
+@pytest.mark.parametrize("G,R,K", [(3, 48, 384), (2, 32, 1024), (1, 16, 128)])
+def test_mx_pack_weight_layout(G, R, K):
+    g = torch.Generator().manual_seed(G * 1000 + R + K)
+    codes = torch.randint(0, 256, (G, R, K // 2), generator=g, dtype=torch.uint8)
+    scales = torch.randint(100, 140, (G, R, K // 32), generator=g, dtype=torch.uint8)
+    pc, ps = B.mx_pack_weight(codes.cuda(), scales.cuda())
+    torch.cuda.synchronize()
+    rc, rs = _np_pack(codes.numpy(), scales.numpy())
+    assert np.array_equal(np_(pc), rc)
+    assert np.array_equal(np_(ps), rs)
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_mx_grouped_ffn(name):
     L = get_layer(SMALL[name])
