@@ -188,93 +188,136 @@ int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E
 
 // ---------------------------------------------------------------- S2 ------
 // One wave per token.  Lane l holds experts l, l+64, l+128, l+192 (E <= 256).
-// k rounds of a wave-wide arg-max over (key desc, id asc); the owner lane
-// retires the winner.  Keys, sigmoid values and weights are fp64.
-struct Cand {
-  double key;
-  int id;
-};
+// Each candidate is an order-preserving unsigned key (the fp32 key in softmax
+// mode, the fp64 key in sigmoid mode; -0 folded into +0, NaN treated as
+// -inf) plus its id; a candidate beats another on a larger key, then on a
+// smaller id.  k rounds of a wave arg-max: each lane's best of its 4, the
+// best of each 16-lane row through 4 DPP exchanges (quad xor 1, quad xor 2,
+// half-row mirror, row mirror), then the 4 row winners read with readlane;
+// the owner retires the winner.  Sigmoid values and weights are fp64.
+__device__ __forceinline__ uint64_t ord_key32(float f) {
+  f = (f != f) ? -__builtin_inff() : f + 0.0f;
+  const uint32_t u = __float_as_uint(f);
+  return (uint64_t)((u >> 31) ? ~u : (u | 0x80000000u));
+}
 
-__device__ __forceinline__ bool better(double ka, int ia, double kb, int ib) {
+__device__ __forceinline__ float unord_key32(uint64_t k) {
+  const uint32_t u = (uint32_t)k;
+  return __uint_as_float((u >> 31) ? (u & 0x7fffffffu) : ~u);
+}
+
+__device__ __forceinline__ uint64_t ord_key64(double d) {
+  d = (d != d) ? -__builtin_inf() : d + 0.0;
+  const uint64_t u = (uint64_t)__double_as_longlong(d);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ bool beats(uint64_t ka, uint32_t ia, uint64_t kb, uint32_t ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_keep_best(uint64_t& k, uint32_t& id) {
+  const uint32_t lo = dpp32<CTRL>((uint32_t)k), hi = dpp32<CTRL>((uint32_t)(k >> 32));
+  const uint32_t oid = dpp32<CTRL>(id);
+  const uint64_t ok = ((uint64_t)hi << 32) | lo;
+  if (beats(ok, oid, k, id)) {
+    k = ok;
+    id = oid;
+  }
+}
+
+__device__ __forceinline__ uint32_t rdlane(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Top-k of one token.  L[i] = logit of expert lane + 64 i (ignored past E).
+// Writes ids[0..k) and weights[0..k) of the token.
 template <int MODE>
-__global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict__ logits,
-                                                        const float* __restrict__ bias, int T,
-                                                        int E, int k, float routed_scale,
-                                                        float eps, int32_t* __restrict__ ids,
-                                                        float* __restrict__ wout) {
+__device__ __forceinline__ void gate_token(const float (&L)[4], const float* __restrict__ bias,
+                                           int E, int k, float routed_scale, float eps,
+                                           int32_t* __restrict__ ids_row,
+                                           float* __restrict__ w_row) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  constexpr int NEG_BIG_ID = 0x7fffffff;
-  const double NEG_INF = -__builtin_inf();
-  double key[4], sval[4];
-  int id[4];
+  constexpr uint32_t NO_ID = 0xffffffffu;
+  uint64_t key[4];
+  uint32_t id[4];
+  double sval[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    key[i] = NEG_INF;
+    key[i] = 0;  // below every real key, even -inf
+    id[i] = NO_ID;
     sval[i] = 0.0;
-    id[i] = NEG_BIG_ID;
     if (e < E) {
-      const float L = logits[(size_t)t * E + e];
-      id[i] = e;
+      id[i] = (uint32_t)e;
       if (MODE == 0) {
-        const float kf = bias ? (L + bias[e]) : L;  // fp32 add, as the oracle
-        key[i] = (kf != kf) ? NEG_INF : (double)kf;
+        key[i] = ord_key32(bias ? (L[i] + bias[e]) : L[i]);  // fp32 add, as the oracle
       } else {
-        const double s = 1.0 / (1.0 + exp(-(double)L));
-        sval[i] = s;
-        const double kk = bias ? s + (double)bias[e] : s;
-        key[i] = (kk != kk) ? NEG_INF : kk;
+        const double sg = 1.0 / (1.0 + exp(-(double)L[i]));
+        sval[i] = sg;
+        key[i] = ord_key64(bias ? sg + (double)bias[e] : sg);
       }
     }
   }
-  double my_key = 0.0, my_s = 0.0;
-  int my_id = 0;
+  uint64_t my_key = 0;
+  uint32_t my_id = 0;
   for (int j = 0; j < k; ++j) {
-    double bk = key[0];
-    int bi = id[0];
-    double bs = sval[0];
+    uint64_t bk = key[0];
+    uint32_t bi = id[0];
 #pragma unroll
     for (int i = 1; i < 4; ++i)
-      if (better(key[i], id[i], bk, bi)) {
+      if (beats(key[i], id[i], bk, bi)) {
         bk = key[i];
         bi = id[i];
-        bs = sval[i];
       }
+    dpp_keep_best<0xB1>(bk, bi);   // quad_perm [1,0,3,2]
+    dpp_keep_best<0x4E>(bk, bi);   // quad_perm [2,3,0,1]
+    dpp_keep_best<0x141>(bk, bi);  // row_half_mirror
+    dpp_keep_best<0x140>(bk, bi);  // row_mirror
+    uint64_t wk = ((uint64_t)rdlane((uint32_t)(bk >> 32), 0) << 32) | rdlane((uint32_t)bk, 0);
+    uint32_t wi = rdlane(bi, 0);
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const double ok = __shfl_xor(bk, d, 64);
-      const int oi = __shfl_xor(bi, d, 64);
-      const double os = __shfl_xor(bs, d, 64);
-      if (better(ok, oi, bk, bi)) {
-        bk = ok;
-        bi = oi;
-        bs = os;
+    for (int r = 1; r < 4; ++r) {
+      const uint64_t rk =
+          ((uint64_t)rdlane((uint32_t)(bk >> 32), 16 * r) << 32) | rdlane((uint32_t)bk, 16 * r);
+      const uint32_t ri = rdlane(bi, 16 * r);
+      if (beats(rk, ri, wk, wi)) {
+        wk = rk;
+        wi = ri;
       }
     }
-    // bi is wave-uniform now; retire it at its owner
+    // wi is wave-uniform; its owner retires it
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (id[i] == bi) {
-        key[i] = NEG_INF;
-        id[i] = NEG_BIG_ID;
+      if (id[i] == wi) {
+        key[i] = 0;
+        id[i] = NO_ID;
       }
     if (lane == j) {
-      my_key = bk;
-      my_id = bi;
-      my_s = bs;
+      my_key = wk;
+      my_id = wi;
     }
   }
   double v;
   if (MODE == 0) {
-    const double k0 = __shfl(my_key, 0, 64);
-    v = (lane < k) ? exp(my_key - k0) : 0.0;
+    const double k0 = (double)unord_key32(__shfl(my_key, 0, 64));
+    v = (lane < k) ? exp((double)unord_key32(my_key) - k0) : 0.0;
   } else {
-    v = (lane < k) ? my_s : 0.0;
+    // the unbiased sigmoid of this lane's winner, from its owner lane
+    const int src = (int)(my_id & 63u), slot = (int)(my_id >> 6);
+    double sv = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double o = __shfl(sval[i], src, 64);
+      if (slot == i) sv = o;
+    }
+    v = (lane < k) ? sv : 0.0;
   }
   double sum = v;
 #pragma unroll
@@ -285,9 +328,27 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
       w = v / sum;
     else
       w = v / (sum + (double)eps) * (double)routed_scale;
-    ids[(size_t)t * k + lane] = my_id;
-    wout[(size_t)t * k + lane] = (float)w;
+    ids_row[lane] = (int32_t)my_id;
+    w_row[lane] = (float)w;
   }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict__ logits,
+                                                        const float* __restrict__ bias, int T,
+                                                        int E, int k, float routed_scale,
+                                                        float eps, int32_t* __restrict__ ids,
+                                                        float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // wave-uniform; no barriers
+  float L[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    L[i] = e < E ? logits[(size_t)t * E + e] : 0.f;
+  }
+  gate_token<MODE>(L, bias, E, k, routed_scale, eps, ids + (size_t)t * k, wout + (size_t)t * k);
 }
 
 int launch_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,
