@@ -60,7 +60,8 @@ _I, _F, _SZ = _c.c_int, _c.c_float, _c.c_size_t
 _P = _c.POINTER
 SIGNATURES = {
     "moe_status_string": (_c.c_char_p, [_I]),
-    "moe_router_logits": (_I, [_vp, _vp, _I, _I, _I, _vp, _vp]),
+    "moe_router_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_router_logits": (_I, [_vp, _vp, _I, _I, _I, _vp, _vp, _SZ, _vp]),
     "moe_gate_topk": (_I, [_vp, _vp, _I, _I, _I, _I, _F, _F, _vp, _vp, _vp]),
     "moe_route_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route": (_I, [_vp, _I, _I, _I, _vp, _vp, _vp, _vp, _vp, _vp, _SZ, _vp]),
@@ -134,7 +135,10 @@ def router_logits(x: torch.Tensor, wr: torch.Tensor, out: Optional[torch.Tensor]
     if out is None:
         out = torch.empty((T, E), dtype=torch.float32, device=x.device)
     _dev(out)
-    _check("moe_router_logits", load().moe_router_logits(_ptr(x), _ptr(wr), T, H, E, _ptr(out), _stream()))
+    nws = int(load().moe_router_workspace_size(T, H, E))
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=x.device) if nws else None
+    _check("moe_router_logits", load().moe_router_logits(_ptr(x), _ptr(wr), T, H, E, _ptr(out),
+                                                         _ptr(ws), nws, _stream()))
     return out
 
 

@@ -138,14 +138,25 @@ const char* moe_status_string(int code) {
   }
 }
 
+size_t moe_router_workspace_size(int T, int H, int E) {
+  if (T <= 0 || check_dims_HE(H, E) != MOE_OK) return 0;
+  return moe::router_workspace_bytes(T, H, E);
+}
+
 int moe_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
-                      void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream) {
   int st;
   if ((st = check_dims_HE(H, E))) return st;
   if (T < 0) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if ((st = check_ptrs({x, wr, logits}))) return st;
-  return moe::launch_router_logits(x, wr, T, H, E, logits, as_stream(stream));
+  const size_t need = moe::router_workspace_bytes(T, H, E);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    if (!al16(workspace)) return MOE_ERR_ALIGN;
+  }
+  return moe::launch_router_logits(x, wr, T, H, E, logits, static_cast<float*>(workspace),
+                                   as_stream(stream));
 }
 
 int moe_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,
@@ -349,7 +360,11 @@ int moe_combine(const uint16_t* y, const int32_t* pair_pos, const float* topk_w,
 
 size_t moe_layer_workspace_size(const MoeLayerDesc* d, int T) {
   if (d == nullptr || T <= 0) return 0;
-  return moe_route_workspace_size(T, d->k, d->E);
+  // the router's partial sums and the routing histograms are live at
+  // different times and share the space
+  const size_t r = moe_router_workspace_size(T, d->H, d->E);
+  const size_t h = moe_route_workspace_size(T, d->k, d->E);
+  return r > h ? r : h;
 }
 
 int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t* out,
@@ -377,16 +392,32 @@ int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t*
     if (!al16(b->workspace)) return MOE_ERR_ALIGN;
   }
   const int k = d->k;
-  if (mx && (st = moe_mx_quantize(x, T, d->H, b->xq, b->xq_scales, stream))) return st;
   const void* xin = mx ? static_cast<const void*>(b->xq) : static_cast<const void*>(x);
   const uint8_t* xin_s = mx ? b->xq_scales : nullptr;
-  if ((st = moe_router_logits(x, d->wr, T, d->H, d->E, b->logits, stream))) return st;
-  if ((st = moe_gate_topk(b->logits, d->bias, T, d->E, k, d->gate_mode, d->routed_scale, d->eps,
-                          b->topk_ids, b->topk_w, stream)))
-    return st;
-  if ((st = moe_route(b->topk_ids, T, k, d->E, b->counts, b->offsets, b->sorted_pair, b->pair_pos,
-                      b->dev_status, b->workspace, b->workspace_bytes, stream)))
-    return st;
+  if (T <= 16 && T * k <= 1024) {
+    // decode: router partials (+ MXFP8 x), then one block for the rest of the routing
+    hipStream_t s = as_stream(stream);
+    float* part = static_cast<float*>(b->workspace);
+    if ((st = moe::launch_router_partial(x, d->wr, T, d->H, d->E, part, mx ? b->xq : nullptr,
+                                         mx ? b->xq_scales : nullptr, s)))
+      return st;
+    if ((st = moe::launch_gate_route_small(part, d->H, d->bias, T, d->E, k, d->gate_mode,
+                                           d->routed_scale, d->eps, b->logits, b->topk_ids,
+                                           b->topk_w, b->counts, b->offsets, b->sorted_pair,
+                                           b->pair_pos, b->dev_status, s)))
+      return st;
+  } else {
+    if (mx && (st = moe_mx_quantize(x, T, d->H, b->xq, b->xq_scales, stream))) return st;
+    if ((st = moe_router_logits(x, d->wr, T, d->H, d->E, b->logits, b->workspace,
+                                b->workspace_bytes, stream)))
+      return st;
+    if ((st = moe_gate_topk(b->logits, d->bias, T, d->E, k, d->gate_mode, d->routed_scale,
+                            d->eps, b->topk_ids, b->topk_w, stream)))
+      return st;
+    if ((st = moe_route(b->topk_ids, T, k, d->E, b->counts, b->offsets, b->sorted_pair,
+                        b->pair_pos, b->dev_status, b->workspace, b->workspace_bytes, stream)))
+      return st;
+  }
   hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(b->ev_ffn_up_begin);
   hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(b->ev_ffn_up_end);
   const bool timed = ev0 != nullptr && ev1 != nullptr;

@@ -9,77 +9,16 @@
 // selection.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mxfmt.hpp"
 
 namespace moe {
 
 // ---------------------------------------------------------------- S1 ------
-// Few tokens (decode): one block of 256 threads per (expert, 16-token tile).
-// Every thread issues all its loads for a 4096-wide slice of H at once (4
-// float4 of the router row, 4 x 8 bytes of each token row), so one memory
-// latency covers the slice; then the block reduces the 16 partial sums
-// (wave butterfly, then the 4 waves through LDS).  Fixed order ->
-// deterministic.
-__global__ __launch_bounds__(256) void router_logits_small(const uint16_t* __restrict__ x,
-                                                           const float* __restrict__ wr, int T,
-                                                           int H, int E,
-                                                           float* __restrict__ logits) {
-  __shared__ float part[4][16];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int e = blockIdx.x;
-  const int t0 = blockIdx.y * 16;
-  const int nt = min(16, T - t0);
-  const float* wrow = wr + (size_t)e * H;
-  const uint16_t* xt = x + (size_t)t0 * H;
-  float acc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  for (int hb = 0; hb < H; hb += 4096) {
-    float4 w4[4];
-    u32x2 xv[4][16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = hb + j * 1024 + tid * 4;
-      const bool ok = h < H;
-      w4[j] = ok ? *reinterpret_cast<const float4*>(wrow + h) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        xv[j][i] = (ok && i < nt) ? *reinterpret_cast<const u32x2*>(xt + (size_t)i * H + h) : u32x2{0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float a = acc[i];
-        a = fmaf(bf16_to_f32(xv[j][i].x & 0xffffu), w4[j].x, a);
-        a = fmaf(bf16_to_f32(xv[j][i].x >> 16), w4[j].y, a);
-        a = fmaf(bf16_to_f32(xv[j][i].y & 0xffffu), w4[j].z, a);
-        a = fmaf(bf16_to_f32(xv[j][i].y >> 16), w4[j].w, a);
-        acc[i] = a;
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float v = acc[i];
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    if (lane == 0) part[wave][i] = v;
-  }
-  __syncthreads();
-  if (tid < nt) logits[(size_t)(t0 + tid) * E + e] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
-}
-
-// Many tokens (prefill): the product on bf16 MFMA, exactly.  Each fp32
-// router weight is split into three bf16 terms, w = hi + mid + lo (hi and mid
-// are truncations, lo is the exact remainder: 8 + 8 + 8 significand bits), so
-// x * w = x*hi + x*mid + x*lo where every product of the bf16 x with a term
-// is exact in fp32; the MFMA accumulates the three products in fp32.  Block
-// tile 32 tokens x 64 experts, K step 32, operands staged in double-buffered
-// LDS (the split is done once, by the loading thread); wave w owns experts
-// 16w..16w+15 of the tile and both 16-token halves (6 MFMAs per K step).
-constexpr int RM_TT = 32, RM_TE = 64;
-
+// Both router kernels compute x . w on bf16 MFMA exactly: each fp32 router
+// weight is split into three bf16 terms, w = hi + mid + lo (hi and mid are
+// truncations, lo is the exact remainder: 8 + 8 + 8 significand bits), so
+// every product of the bf16 x with a term is exact in fp32 and the MFMA
+// accumulates the three products in fp32.
 __device__ __forceinline__ void split3_bf16(const float* w8, u32x4& hi, u32x4& mid, u32x4& lo) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -101,6 +40,132 @@ __device__ __forceinline__ void split3_bf16(const float* w8, u32x4& hi, u32x4& m
     lo[q] = l2;
   }
 }
+
+// Few tokens (decode): split over H.  A wave computes the partial logits of
+// 16 tokens x 16 experts over one 256-wide slice of H (8 K-steps, all loads
+// issued at once: one memory round trip) and stores them to
+// partial[slice][t][e]; the slices are summed in slice order afterwards
+// (router_reduce, or the fused gate), so the result is deterministic.
+// Grid (ceil(E/64), H/256, ceil(T/16)), wave w of block b: experts
+// 16*(4b + w) ...  With xq != nullptr the waves also write the MXFP8
+// quantisation of their x slice (each MX block of 32 is held by the 4 lanes
+// of one token; the expert groups of a slice split its steps), so the W4A8
+// path needs no separate quantiser launch.
+constexpr int RP_HS = 256;
+
+size_t router_workspace_bytes(int T, int H, int E) {
+  if (T > 64) return 0;
+  return (size_t)(H / RP_HS) * (size_t)T * (size_t)E * sizeof(float);
+}
+
+__global__ __launch_bounds__(256) void router_partial(const uint16_t* __restrict__ x,
+                                                      const float* __restrict__ wr, int T, int H,
+                                                      int E, float* __restrict__ partial,
+                                                      uint8_t* __restrict__ xq,
+                                                      uint8_t* __restrict__ xq_scales) {
+  const int lane = threadIdx.x & 63;
+  const int eg = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int e0 = eg * 16;
+  if (e0 >= E) return;  // wave-uniform; the kernel has no barriers
+  const int sl = blockIdx.y, h0 = sl * RP_HS, t0 = blockIdx.z * 16;
+  const int fr = lane & 15, fc = lane >> 4;
+  const int t = min(t0 + fr, T - 1);  // rows past T reuse a valid row
+  const int e = min(e0 + fr, E - 1);
+  const uint16_t* xp = x + (size_t)t * H + h0 + fc * 8;
+  const float* wp = wr + (size_t)e * H + h0 + fc * 8;
+  u32x4 xa[8];
+  float4 wa[8][2];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    xa[st] = ld16(xp + st * 32);
+    wa[st][0] = *reinterpret_cast<const float4*>(wp + st * 32);
+    wa[st][1] = *reinterpret_cast<const float4*>(wp + st * 32 + 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first use
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const float w8[8] = {wa[st][0].x, wa[st][0].y, wa[st][0].z, wa[st][0].w,
+                         wa[st][1].x, wa[st][1].y, wa[st][1].z, wa[st][1].w};
+    u32x4 h, m, l;
+    split3_bf16(w8, h, m, l);
+    acc = mfma16x16x32(xa[st], h, acc);
+    acc = mfma16x16x32(xa[st], m, acc);
+    acc = mfma16x16x32(xa[st], l, acc);
+  }
+  // D[m][n]: lane holds expert e0 + fr, tokens t0 + 4*fc + i
+  if (e0 + fr < E) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = t0 + 4 * fc + i;
+      if (tt < T) partial[((size_t)sl * T + tt) * E + e0 + fr] = acc[i];
+    }
+  }
+  if (xq != nullptr) {
+    // lane (fr, fc) holds x[t][h0 + 32 st + 8 fc .. +8]: lanes fr, fr+16,
+    // fr+32, fr+48 together hold one MX block of token t per step.  The
+    // expert groups of a slice share its 8 steps (group g quantises the
+    // steps st with st % groups == g % groups).
+    const int ngroups = (E + 15) / 16;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st % ngroups != eg % ngroups) continue;  // wave-uniform
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[2 * q] = bf16_to_f32(xa[st][q] & 0xffffu);
+        f[2 * q + 1] = bf16_to_f32(xa[st][q] >> 16);
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const int ex = mx_exponent(amax);
+      const float inv = exp2_neg(ex);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= e4m3_encode(f[i] * inv) << (8 * i);
+        hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
+      }
+      if (t0 + fr < T) {
+        const int col = h0 + 32 * st + 8 * fc;
+        *reinterpret_cast<u32x2*>(xq + (size_t)(t0 + fr) * H + col) = u32x2{lo, hi};
+        if (fc == 0) xq_scales[(size_t)(t0 + fr) * (H / 32) + col / 32] = (uint8_t)(ex + 127);
+      }
+    }
+  }
+}
+
+// Sum of the S slice partials of one logit, in slice order; the loads of 8
+// slices are issued together so that S slices cost S/8 memory round trips.
+__device__ __forceinline__ float sum_slices(const float* __restrict__ p, int S, size_t stride) {
+  float v = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float q[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) q[u] = s0 + u < S ? p[(size_t)(s0 + u) * stride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) v = (s0 + u == 0) ? q[u] : v + q[u];
+  }
+  return v;
+}
+
+// logits[t][e] = sum over slices, in slice order.
+__global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ partial, int S,
+                                                     int T, int E, float* __restrict__ logits) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= T * E) return;
+  logits[i] = sum_slices(partial + i, S, (size_t)T * E);
+}
+
+// Many tokens (prefill): block tile 32 tokens x 64 experts, K step 32,
+// operands staged in double-buffered LDS (the split is done once, by the
+// loading thread); wave w owns experts 16w..16w+15 of the tile and both
+// 16-token halves (6 MFMAs per K step).
+constexpr int RM_TT = 32, RM_TE = 64;
 
 __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wr, int T,
@@ -174,11 +239,19 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
   }
 }
 
+int launch_router_partial(const uint16_t* x, const float* wr, int T, int H, int E,
+                          float* partial, uint8_t* xq, uint8_t* xq_scales, hipStream_t s) {
+  hipLaunchKernelGGL(router_partial, dim3((E + 63) / 64, H / RP_HS, (T + 15) / 16), dim3(256), 0,
+                     s, x, wr, T, H, E, partial, xq, xq_scales);
+  return launch_status();
+}
+
 int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
-                         hipStream_t s) {
+                         float* ws, hipStream_t s) {
   if (T <= 64) {
-    hipLaunchKernelGGL(router_logits_small, dim3(E, (T + 15) / 16), dim3(256), 0, s, x, wr, T, H,
-                       E, logits);
+    launch_router_partial(x, wr, T, H, E, ws, nullptr, nullptr, s);
+    hipLaunchKernelGGL(router_reduce, dim3((T * E + 255) / 256), dim3(256), 0, s, ws, H / RP_HS,
+                       T, E, logits);
   } else {
     hipLaunchKernelGGL(router_logits_mfma, dim3((T + RM_TT - 1) / RM_TT, (E + RM_TE - 1) / RM_TE),
                        dim3(256), 0, s, x, wr, T, H, E, logits);
@@ -236,10 +309,34 @@ __device__ __forceinline__ uint32_t rdlane(uint32_t v, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
 }
 
+// Softmax mode: key and id packed into one u64, (ord(key) << 32) | ~id, so
+// that "better" is plain unsigned order.  Wave max: 4 in-row DPP exchanges,
+// then row_bcast15 (rows 1, 3 take lane 15 of the row before) and row_bcast31
+// (rows 2, 3 take lane 31): lane 63 ends with the wave's maximum.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void dpp_max_u64(uint64_t& v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v,
+                                                            CTRL, ROWS, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(
+      (int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xF, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  v = o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  dpp_max_u64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  dpp_max_u64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  dpp_max_u64<0x141, 0xF>(v);  // row_half_mirror
+  dpp_max_u64<0x140, 0xF>(v);  // row_mirror
+  dpp_max_u64<0x142, 0xA>(v);  // row_bcast15
+  dpp_max_u64<0x143, 0xC>(v);  // row_bcast31
+  return ((uint64_t)rdlane((uint32_t)(v >> 32), 63) << 32) | rdlane((uint32_t)v, 63);
+}
+
 // Top-k of one token.  L[i] = logit of expert lane + 64 i (ignored past E).
 // Writes ids[0..k) and weights[0..k) of the token.
 template <int MODE>
-__device__ __forceinline__ void gate_token(const float (&L)[4], const float* __restrict__ bias,
+__device__ __forceinline__ uint32_t gate_token(const float (&L)[4], const float* __restrict__ bias,
                                            int E, int k, float routed_scale, float eps,
                                            int32_t* __restrict__ ids_row,
                                            float* __restrict__ w_row) {
@@ -267,7 +364,23 @@ __device__ __forceinline__ void gate_token(const float (&L)[4], const float* __r
   }
   uint64_t my_key = 0;
   uint32_t my_id = 0;
-  for (int j = 0; j < k; ++j) {
+  if (MODE == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = key[i] ? ((key[i] << 32) | (NO_ID - id[i])) : 0;
+    for (int j = 0; j < k; ++j) {
+      uint64_t b = key[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) b = key[i] > b ? key[i] : b;
+      const uint64_t w = wave_max_u64(b);  // wave-uniform; keys are unique (ids differ)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) key[i] = key[i] == w ? 0 : key[i];
+      if (lane == j) {
+        my_key = w >> 32;
+        my_id = NO_ID - (uint32_t)w;
+      }
+    }
+  }
+  for (int j = 0; MODE == 1 && j < k; ++j) {
     uint64_t bk = key[0];
     uint32_t bi = id[0];
 #pragma unroll
@@ -331,6 +444,7 @@ __device__ __forceinline__ void gate_token(const float (&L)[4], const float* __r
     ids_row[lane] = (int32_t)my_id;
     w_row[lane] = (float)w;
   }
+  return my_id;  // lanes < k: the expert of slot lane
 }
 
 template <int MODE>
@@ -349,6 +463,122 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
     L[i] = e < E ? logits[(size_t)t * E + e] : 0.f;
   }
   gate_token<MODE>(L, bias, E, k, routed_scale, eps, ids + (size_t)t * k, wout + (size_t)t * k);
+}
+
+// --------------------------------------------------- S1+S2+S3/S4, decode ---
+// Few tokens (T <= 16, T*k <= 1024): one block of 1024 threads finishes the
+// routing in one launch after router_partial.  Wave t sums token t's slice
+// partials (slice order, as router_reduce) into its logits, stores them and
+// runs the top-k of gate_token; then the block does init_routing and the
+// expert-token counts ([Qwen3] "GMM enablement and routing optimisation") for
+// the T*k pairs, one pair per thread: within a wave, pairs with the same
+// expert are matched with ballots over the 8 id bits and ranked by lane;
+// across waves through per-wave counts in LDS; expert bases are the exclusive
+// scan of the counts.  The order (expert, then pair index) is the stable
+// counting sort of the standalone route kernels.
+template <int MODE>
+__global__ __launch_bounds__(1024) void gate_route_small(
+    const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E, int k,
+    float routed_scale, float eps, float* __restrict__ logits, int32_t* __restrict__ ids,
+    float* __restrict__ wout, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos,
+    int32_t* __restrict__ dev_status) {
+  __shared__ int wcnt[16][256];
+  __shared__ int base[256];
+  __shared__ int wsum[4];
+  __shared__ int sids[1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (wave < T) {
+    // the partials were written by other CUs (other L2s): issue every load
+    // of this lane (up to 4 experts x 16 slices) before the first add
+    float L[4] = {0.f, 0.f, 0.f, 0.f};
+    const size_t stride = (size_t)T * E;
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      float q[4][16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          q[i][u] = (e < E && s0 + u < S) ? partial[(size_t)(s0 + u) * stride + (size_t)wave * E + e]
+                                          : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (s0 + u < S) L[i] = (s0 + u == 0) ? q[i][u] : L[i] + q[i][u];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) logits[(size_t)wave * E + e] = L[i];
+    }
+    const uint32_t my = gate_token<MODE>(L, bias, E, k, routed_scale, eps,
+                                         ids + (size_t)wave * k, wout + (size_t)wave * k);
+    if (lane < k) sids[wave * k + lane] = (int)my;
+  }
+  for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  const int R = T * k;
+  const int p = tid;
+  const int e = p < R ? sids[p] : -1;
+  const bool ok = e >= 0 && e < E;
+  unsigned long long match = __ballot(ok);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const bool on = ok && ((e >> bit) & 1);
+    const unsigned long long bb = __ballot(on);
+    match &= ((e >> bit) & 1) ? bb : ~bb;
+  }
+  const int rank = __popcll(match & ((1ull << lane) - 1ull));
+  if (ok && rank == 0) wcnt[wave][e] = __popcll(match);
+  __syncthreads();
+  // per-expert totals and their exclusive scan (threads 0..255, E <= 256)
+  int v = 0, incl = 0;
+  if (tid < E)
+    for (int w = 0; w < 16; ++w) v += wcnt[w][tid];
+  if (tid < 256) {  // waves 0..3, whole waves
+    incl = wave_incl_scan(v);
+    if (lane == 63) wsum[wave] = incl;
+  }
+  __syncthreads();
+  if (tid < E) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int excl = before + incl - v;
+    base[tid] = excl;
+    counts[tid] = v;
+    offsets[tid] = excl;
+    if (tid == E - 1) offsets[E] = excl + v;
+  }
+  __syncthreads();
+  if (ok) {
+    int pos = base[e] + rank;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+    sorted_pair[pos] = p;
+    pair_pos[p] = pos;
+  } else if (p < R) {
+    pair_pos[p] = -1;
+  }
+  const bool bad = __syncthreads_or(p < R && !ok);
+  if (tid == 0 && dev_status != nullptr) *dev_status = bad ? 1 : 0;
+}
+
+int launch_gate_route_small(const float* partial, int H, const float* bias, int T, int E, int k,
+                            int mode, float routed_scale, float eps, float* logits, int32_t* ids,
+                            float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                            int32_t* pair_pos, int32_t* dev_status, hipStream_t s) {
+  const int S = H / RP_HS;
+  if (mode == 0)
+    hipLaunchKernelGGL(gate_route_small<0>, dim3(1), dim3(1024), 0, s, partial, S, bias, T, E, k,
+                       routed_scale, eps, logits, ids, w, counts, offsets, sorted_pair, pair_pos,
+                       dev_status);
+  else
+    hipLaunchKernelGGL(gate_route_small<1>, dim3(1), dim3(1024), 0, s, partial, S, bias, T, E, k,
+                       routed_scale, eps, logits, ids, w, counts, offsets, sorted_pair, pair_pos,
+                       dev_status);
+  return launch_status();
 }
 
 int launch_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,

@@ -17,8 +17,20 @@ inline int launch_status() { return hipGetLastError() == hipSuccess ? 0 : -5; }
 // runs once per (kernel, device) and is cached.
 int resident_grid(const void* kernel, int block, long long max_tiles);
 
+// Router workspace (bytes) for T tokens: the split-H partial logits of the
+// few-token path (T <= 64), else 0.
+size_t router_workspace_bytes(int T, int H, int E);
 int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
-                         hipStream_t s);
+                         float* ws, hipStream_t s);
+// Few-token layer front end: partial logits (+ MXFP8 x when xq != nullptr),
+// then one block for logits, top-k, counts and the permutation (T <= 16,
+// T*k <= 1024).
+int launch_router_partial(const uint16_t* x, const float* wr, int T, int H, int E,
+                          float* partial, uint8_t* xq, uint8_t* xq_scales, hipStream_t s);
+int launch_gate_route_small(const float* partial, int H, const float* bias, int T, int E, int k,
+                            int mode, float routed_scale, float eps, float* logits, int32_t* ids,
+                            float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                            int32_t* pair_pos, int32_t* dev_status, hipStream_t s);
 int launch_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,
                      float routed_scale, float eps, int32_t* ids, float* w, hipStream_t s);
 

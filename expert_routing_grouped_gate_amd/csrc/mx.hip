@@ -27,47 +27,11 @@
 // (32-column blocks) before storing.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mxfmt.hpp"
 
 namespace moe {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-// E4M3FN code of v (already divided by its block scale), RNE, saturating.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t bits = __float_as_uint(v);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = __uint_as_float(bits & 0x7fffffffu);
-  if (!(a < 448.f)) return sign | 0x7eu;  // saturate (also catches NaN)
-  if (a < 0.015625f) {                    // below 2^-6: subnormal grid 2^-9
-    const uint32_t m = (uint32_t)rintf(a * 512.f);  // 0..8; 8 is 2^-6 = code 0x08
-    return sign | m;
-  }
-  int E = (int)((bits >> 23) & 0xffu) - 127;  // floor(log2 a), -6..8
-  const float q = __uint_as_float((uint32_t)(127 + 3 - E) << 23) * a;  // a * 2^(3-E) in [8,16)
-  uint32_t m = (uint32_t)rintf(q);
-  if (m == 16u) {
-    m = 8u;
-    ++E;
-  }
-  uint32_t code = ((uint32_t)(E + 7) << 3) | (m - 8u);
-  if (code > 0x7eu) code = 0x7eu;
-  return sign | code;
-}
-
-// floor(log2(amax)) - 8, clamped to [-127, 127]; amax zero or subnormal -> -127.
-__device__ __forceinline__ int mx_exponent(float amax) {
-  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xffu);
-  if (ef == 0) return -127;
-  const int e = ef - 127 - 8;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-// 2^-e as an fp32 (e in [-127, 127]; 2^127 is finite, 2^-127 is subnormal).
-__device__ __forceinline__ float exp2_neg(int e) {
-  const int p = -e;
-  if (p >= -126) return __uint_as_float((uint32_t)(p + 127) << 23);
-  return __uint_as_float(1u << (p + 149));  // subnormal powers of two
-}
 
 // ------------------------------------------------------------ S0 quant ---
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, int rows,

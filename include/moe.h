@@ -82,9 +82,13 @@ const char* moe_status_string(int code);
  *   x      [T, H] bf16
  *   wr     [E, H] fp32
  *   logits [T, E] fp32 (output)
+ *   workspace  device scratch of moe_router_workspace_size(T, H, E) bytes
+ *              (few tokens: per-slice partial sums over H; may be NULL when
+ *              that size is 0); MOE_ERR_WORKSPACE when too small.
  * Deterministic: the summation order of each output is fixed. */
+size_t moe_router_workspace_size(int T, int H, int E);
 int moe_router_logits(const uint16_t* x, const float* wr, int T, int H, int E,
-                      float* logits, void* stream);
+                      float* logits, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------- S2 -----
  * Gate top-k ([Qwen3] gating top-k softmax; [Hy3] section 1.3 router call
@@ -237,7 +241,10 @@ int moe_combine(const uint16_t* y, const int32_t* pair_pos, const float* topk_w,
                 void* stream);
 
 /* ------------------------------------------------------ whole layer -----
- * S0..S7 in one call on one stream. */
+ * S0..S7 in one call on one stream.  With T <= 16 and T*k <= 1024 (decode)
+ * the front end is two launches: router partial sums (which also write the
+ * MXFP8 x of the W4A8 path) and one block for logits, top-k, counts and the
+ * permutation; the buffers receive the same values as the per-step calls. */
 typedef struct {
   int H, E, k;
   int gate_mode;        /* moe_gate_mode */
@@ -266,7 +273,9 @@ typedef struct {
   void* shared_act;       /* [T, shared_I] when the layer has a shared expert */
   uint8_t* shared_act_scales;
   uint16_t* shared_y;     /* [T, H] */
-  void* workspace;        /* moe_layer_workspace_size(desc, T) bytes */
+  void* workspace;        /* moe_layer_workspace_size(desc, T) bytes (router
+                             partial sums or routing histograms; one call at
+                             a time per workspace) */
   size_t workspace_bytes;
   /* Optional hipEvent_t handles, recorded on `stream` right before and right
    * after the grouped GEMM1 (w13 + SwiGLU) launch so that a caller can time

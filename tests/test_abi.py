@@ -56,12 +56,19 @@ MIS = FAKE + 4          # misaligned
 
 def test_router_logits_checks(lib):
     f = lib.moe_router_logits
-    assert f(None, FAKE, 4, 256, 8, FAKE, None) == NULL
-    assert f(FAKE, FAKE, 4, 255, 8, FAKE, None) == UNSUP        # H % 256
-    assert f(FAKE, FAKE, 4, 256, 257, FAKE, None) == UNSUP      # E > 256
-    assert f(FAKE, FAKE, -1, 256, 8, FAKE, None) == SHAPE
-    assert f(MIS, FAKE, 4, 256, 8, FAKE, None) == ALIGN
-    assert f(None, None, 0, 256, 8, None, None) == OK           # T == 0: nothing to do
+    ws = lib.moe_router_workspace_size(4, 256, 8)
+    assert ws == 1 * 4 * 8 * 4                                   # one 256-wide slice of partials
+    assert lib.moe_router_workspace_size(4, 4096, 128) == 16 * 4 * 128 * 4
+    assert lib.moe_router_workspace_size(65, 4096, 128) == 0    # many tokens: no partials
+    assert f(None, FAKE, 4, 256, 8, FAKE, FAKE, ws, None) == NULL
+    assert f(FAKE, FAKE, 4, 255, 8, FAKE, FAKE, ws, None) == UNSUP        # H % 256
+    assert f(FAKE, FAKE, 4, 256, 257, FAKE, FAKE, ws, None) == UNSUP      # E > 256
+    assert f(FAKE, FAKE, -1, 256, 8, FAKE, FAKE, ws, None) == SHAPE
+    assert f(MIS, FAKE, 4, 256, 8, FAKE, FAKE, ws, None) == ALIGN
+    assert f(FAKE, FAKE, 4, 256, 8, FAKE, None, 0, None) == WS           # partials need space
+    assert f(FAKE, FAKE, 4, 256, 8, FAKE, FAKE, ws - 4, None) == WS
+    assert f(FAKE, FAKE, 4, 256, 8, FAKE, MIS, ws, None) == ALIGN
+    assert f(None, None, 0, 256, 8, None, None, 0, None) == OK           # T == 0: nothing to do
 
 
 def test_gate_topk_checks(lib):
@@ -121,7 +128,9 @@ def test_layer_forward_checks(lib):
     assert f(ctypes.byref(d), FAKE, 4, FAKE, ctypes.byref(b), None) == NULL   # buffers unset
     d2 = B.MoeLayerDesc(512, 8, 2, 0, 1.0, 1e-20, FAKE, None, w)
     assert f(ctypes.byref(d2), FAKE, 4, FAKE, ctypes.byref(b), None) == SHAPE  # H mismatch
-    assert lib.moe_layer_workspace_size(ctypes.byref(d), 16) == 0
+    # 16 tokens: the router's partial sums (1 slice x 16 x 8 fp32)
+    assert lib.moe_layer_workspace_size(ctypes.byref(d), 16) == 16 * 8 * 4
+    assert lib.moe_layer_workspace_size(ctypes.byref(d), 100) == 0
 
 
 def test_mx_pack_checks_and_sizes(lib):

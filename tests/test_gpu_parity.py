@@ -26,6 +26,9 @@ SMALL = {
     "small_hy3": CFG["hy3"].with_(name="small_hy3", T=301, H=256, I=128, shared_I=128, x_seed=13),
     "small_hy3_decode": CFG["hy3"].with_(name="small_hy3_decode", T=9, H=256, I=128, shared_I=128, x_seed=14),
     "wide_k": CFG["tiny"].with_(name="wide_k", T=40, E=256, k=32, I=128, x_seed=15, family_seed=1099),
+    # decode-sized (T <= 16): the layer's two-launch routing front end
+    "wide_k_decode": CFG["tiny"].with_(name="wide_k_decode", T=16, E=256, k=32, I=128, x_seed=16,
+                                       family_seed=1099),
 }
 
 
@@ -221,9 +224,30 @@ def _layer_check(cfg, tokens=None):
     return out
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_T1", "small_prefill", "small_hy3", "small_hy3_decode", "wide_k"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_T1", "small_prefill", "small_hy3", "small_hy3_decode", "wide_k",
+                                  "wide_k_decode"])
 def test_layer_small(name):
     _layer_check(SMALL[name])
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_hy3_decode", "wide_k_decode"])
+def test_decode_front_end_equals_the_step_calls(name):
+    """With T <= 16 the layer routes with two launches (router partial sums,
+    then one block for logits, top-k, counts and permutation); its buffers
+    must equal the standalone router, gate and route calls bit for bit."""
+    L = get_layer(SMALL[name])
+    cfg = L.cfg
+    layer = L.layer()
+    layer.forward(L.dev["x"])
+    b = layer.buf
+    logits = B.router_logits(L.dev["x"], L.dev["wr"])
+    ids, w = B.gate_topk(logits, cfg.k, L.mode, L.dev["bias"], cfg.routed_scale, cfg.eps)
+    counts, offsets, sp, pp = B.route(ids, cfg.E)
+    torch.cuda.synchronize()
+    assert torch.equal(b["logits"], logits)
+    assert torch.equal(b["topk_ids"], ids) and torch.equal(b["topk_w"], w)
+    for key, ref in (("counts", counts), ("offsets", offsets), ("sorted_pair", sp), ("pair_pos", pp)):
+        assert torch.equal(b[key], ref), key
 
 
 def test_layer_zero_tokens():
