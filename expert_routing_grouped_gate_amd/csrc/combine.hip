@@ -20,6 +20,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ shared_y, int k,
                                                       int H, uint16_t* __restrict__ out) {
   const int t = blockIdx.x;
+  const int R = (int)gridDim.x * k;
   const int c = blockIdx.y * CB_COLS + threadIdx.x * 8;
   if (c >= H) return;  // no barriers below
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -29,7 +30,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     int pos[8];
     u32x4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) pos[u] = j0 + u < k ? pp[j0 + u] : -1;
+    for (int u = 0; u < 8; ++u) {
+      pos[u] = j0 + u < k ? pp[j0 + u] : -1;
+      if (pos[u] >= R) pos[u] = -1;  // outside the rows of y: treated as dropped
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       v[u] = pos[u] >= 0 ? ld16(y + (size_t)pos[u] * H + c) : u32x4{0u, 0u, 0u, 0u};

@@ -57,6 +57,15 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * base + (xcd < rem ? xcd : rem) + local;
 }
 
+// Activation row of sorted row r: the token of pair sorted_pair[r] when
+// gathering (clamped into [0, rows/topk)), else r itself.
+__device__ __forceinline__ int gather_row(const int32_t* __restrict__ sorted_pair, int gather,
+                                          int topk, int total_rows, int r) {
+  if (!gather) return r;
+  const int t = max(sorted_pair[r], 0) / topk;
+  return min(t, total_rows / topk - 1);
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -81,7 +90,10 @@ struct TileMap {
   const int* offsets;
   int ident_rows;
 
-  __device__ __forceinline__ void init(const int* __restrict__ offs, int G, int ident, int bm) {
+  // Offsets are clamped to [0, max_rows] (max_rows: rows the output can
+  // hold), so even malformed offsets yield tiles inside the buffers.
+  __device__ __forceinline__ void init(const int* __restrict__ offs, int G, int ident, int bm,
+                                       int max_rows) {
     offsets = offs;
     ident_rows = ident;
     BM = bm;
@@ -93,11 +105,11 @@ struct TileMap {
     per = (G + 63) >> 6;
     gbeg = lane * per;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) o[i] = offs[min(gbeg + i, G)];
+    for (int i = 0; i < 6; ++i) o[i] = min(max(offs[min(gbeg + i, G)], 0), max_rows);
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
-      const int t = (i < per && gbeg + i < G) ? (o[i + 1] - o[i] + bm - 1) / bm : 0;
+      const int t = (i < per && gbeg + i < G) ? max(o[i + 1] - o[i] + bm - 1, 0) / bm : 0;
       tiles[i] = t;
       sum += t;
     }

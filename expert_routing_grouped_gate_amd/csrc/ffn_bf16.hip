@@ -36,7 +36,7 @@ __device__ __forceinline__ void skinny_tile(const GroupedGemm& g, int lane, int 
   const int kq = (lane >> 4) * 8;  // this lane's 8 k values inside a 32-step
   const int n0 = n_tile * 16 * WN + wn * 16;
   const int r = row0 + min(li, nrows - 1);  // rows past the tile end reuse a valid row
-  const int arow = g.gather ? g.sorted_pair[r] / g.topk : r;
+  const int arow = gather_row(g.sorted_pair, g.gather, g.topk, g.total_rows, r);
   const int K = g.K;
   const int Kw = K / WK;
   const int kbeg = wk * Kw;
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(64 * WN * WK) void ffn_skinny(GroupedGemm g, int n_
   const int wn = wave % WN;
   const int wk = wave / WN;
   TileMap tm;
-  tm.init(g.offsets, g.G, g.ident_rows, 16);
+  tm.init(g.offsets, g.G, g.ident_rows, 16, g.total_rows);
   const int total = tm.total * n_tiles;
   // persistent: block b takes tiles b, b + gridDim.x, ... (gridDim.x % 8 == 0
   // keeps every tile of a block on the block's XCD)
@@ -224,7 +224,7 @@ __device__ __forceinline__ void tiled_tile(const GroupedGemm& g, u32x4* smem, in
     const int c = (lane & 7) ^ (lane >> 3);
     if (row < BM) {
       const int r = row0 + min(row, nrows - 1);
-      const int arow = g.gather ? g.sorted_pair[r] / g.topk : r;
+      const int arow = gather_row(g.sorted_pair, g.gather, g.topk, g.total_rows, r);
       src[i] = static_cast<const uint16_t*>(g.A) + (size_t)arow * K + c * 8;
     } else {
       const int br = row - BM;
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void ffn_tiled(GroupedGemm g, in
   using C = Tiled<SWIGLU, BM, BN, WM, WN, NS>;
   __shared__ u32x4 smem[C::NSTAGE * C::STAGE];
   TileMap tm;
-  tm.init(g.offsets, g.G, g.ident_rows, BM);
+  tm.init(g.offsets, g.G, g.ident_rows, BM, g.total_rows);
   const int total = tm.total * n_tiles;
   // Tile order: expert-major, then n-tile, then the expert's m-tiles.  The
   // m-tiles that share a weight tile are neighbours (they start together and

@@ -46,8 +46,9 @@ __device__ __forceinline__ void split3_bf16(const float* w8, u32x4& hi, u32x4& m
 // issued at once: one memory round trip) and stores them to
 // partial[slice][t][e]; the slices are summed in slice order afterwards
 // (router_reduce, or the fused gate), so the result is deterministic.
-// Grid (ceil(E/64), H/256, ceil(T/16)), wave w of block b: experts
-// 16*(4b + w) ...  With xq != nullptr the waves also write the MXFP8
+// Grid (ceil(E/16), H/256, ceil(T/16)) of one-wave blocks (the 2 MB of Wr is
+// spread over as many CUs as possible), block b: experts 16b ...  With
+// xq != nullptr the waves also write the MXFP8
 // quantisation of their x slice (each MX block of 32 is held by the 4 lanes
 // of one token; the expert groups of a slice split its steps), so the W4A8
 // path needs no separate quantiser launch.
@@ -58,13 +59,13 @@ size_t router_workspace_bytes(int T, int H, int E) {
   return (size_t)(H / RP_HS) * (size_t)T * (size_t)E * sizeof(float);
 }
 
-__global__ __launch_bounds__(256) void router_partial(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(64) void router_partial(const uint16_t* __restrict__ x,
                                                       const float* __restrict__ wr, int T, int H,
                                                       int E, float* __restrict__ partial,
                                                       uint8_t* __restrict__ xq,
                                                       uint8_t* __restrict__ xq_scales) {
   const int lane = threadIdx.x & 63;
-  const int eg = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int eg = blockIdx.x;
   const int e0 = eg * 16;
   if (e0 >= E) return;  // wave-uniform; the kernel has no barriers
   const int sl = blockIdx.y, h0 = sl * RP_HS, t0 = blockIdx.z * 16;
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
 
 int launch_router_partial(const uint16_t* x, const float* wr, int T, int H, int E,
                           float* partial, uint8_t* xq, uint8_t* xq_scales, hipStream_t s) {
-  hipLaunchKernelGGL(router_partial, dim3((E + 63) / 64, H / RP_HS, (T + 15) / 16), dim3(256), 0,
+  hipLaunchKernelGGL(router_partial, dim3((E + 15) / 16, H / RP_HS, (T + 15) / 16), dim3(64), 0,
                      s, x, wr, T, H, E, partial, xq, xq_scales);
   return launch_status();
 }

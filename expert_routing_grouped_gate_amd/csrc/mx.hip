@@ -189,7 +189,7 @@ __device__ __forceinline__ MxTile mx_tile_at(const GroupedGemm& g, const TileMap
   t.nrows = __builtin_amdgcn_readfirstlane(nrows);
   t.n0 = __builtin_amdgcn_readfirstlane(n_tile * (SWIGLU ? 32 : 64));
   const int r = t.row0 + min(li, t.nrows - 1);  // rows past the tile end reuse a valid row
-  const int arow = g.gather ? g.sorted_pair[r] / g.topk : r;
+  const int arow = gather_row(g.sorted_pair, g.gather, g.topk, g.total_rows, r);
   t.xa = static_cast<const uint8_t*>(g.A) + (size_t)arow * g.K + 16 * kb;
   t.xs = g.A_scales + (size_t)arow * (g.K / 32);
   t.live = 1;
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256) void ffn_mx_stream(GroupedGemm g, int n_tiles)
   // scalar offsets in scalar registers)
   const int gw = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) * gridDim.x + blockIdx.x);
   TileMap tm;
-  tm.init(g.offsets, g.G, g.ident_rows, 16);
+  tm.init(g.offsets, g.G, g.ident_rows, 16, g.total_rows);
   const int total = __builtin_amdgcn_readfirstlane(tm.total * n_tiles);
   if (gw >= total) return;  // the kernel has no barriers
   const int nb = g.K / 128 / U;
