@@ -11,6 +11,8 @@
 #include "launch.hpp"
 #include "mxfmt.hpp"
 
+#include <type_traits>
+
 namespace moe {
 
 // ---------------------------------------------------------------- S1 ------
@@ -261,22 +263,24 @@ int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E
 }
 
 // ---------------------------------------------------------------- S2 ------
-// One wave per token.  Lane l holds experts l, l+64, l+128, l+192 (E <= 256).
-// Each candidate is an order-preserving unsigned key (the fp32 key in softmax
-// mode, the fp64 key in sigmoid mode; -0 folded into +0, NaN treated as
-// -inf) plus its id; a candidate beats another on a larger key, then on a
-// smaller id.  k rounds of a wave arg-max: each lane's best of its 4, the
-// best of each 16-lane row through 4 DPP exchanges (quad xor 1, quad xor 2,
-// half-row mirror, row mirror), then the 4 row winners read with readlane;
-// the owner retires the winner.  Sigmoid values and weights are fp64.
-__device__ __forceinline__ uint64_t ord_key32(float f) {
+// One wave per token.  Lane l holds experts l + 64 i, i < NSL = ceil(E/64).
+// Each candidate has an order-preserving unsigned key (softmax: the fp32
+// key; sigmoid: the fp64 key as hi:lo words), -0 folded into +0 and NaN
+// treated as -inf; a candidate beats another on a larger key, then on a
+// smaller id.  Each of the k rounds: the wave maximum of the (high) key word
+// with v_max_u32 over DPP (quad xor 1 and 2, half-row and row mirror,
+// row_bcast15 and row_bcast31; lane 63 ends with the maximum); in sigmoid
+// mode the same for the low word among the candidates that reach the high
+// maximum; then the smallest id holding the maximum from ballots, slot by
+// slot (ids ascend with the slot, then the lane).  The owner retires it.
+// 32-bit operations only, no per-round LDS traffic.  Weights are fp64.
+__device__ __forceinline__ uint32_t ord_key32(float f) {
   f = (f != f) ? -__builtin_inff() : f + 0.0f;
   const uint32_t u = __float_as_uint(f);
-  return (uint64_t)((u >> 31) ? ~u : (u | 0x80000000u));
+  return (u >> 31) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float unord_key32(uint64_t k) {
-  const uint32_t u = (uint32_t)k;
+__device__ __forceinline__ float unord_key32(uint32_t u) {
   return __uint_as_float((u >> 31) ? (u & 0x7fffffffu) : ~u);
 }
 
@@ -286,136 +290,112 @@ __device__ __forceinline__ uint64_t ord_key64(double d) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-__device__ __forceinline__ bool beats(uint64_t ka, uint32_t ia, uint64_t kb, uint32_t ib) {
-  return ka > kb || (ka == kb && ia < ib);
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-
-template <int CTRL>
-__device__ __forceinline__ void dpp_keep_best(uint64_t& k, uint32_t& id) {
-  const uint32_t lo = dpp32<CTRL>((uint32_t)k), hi = dpp32<CTRL>((uint32_t)(k >> 32));
-  const uint32_t oid = dpp32<CTRL>(id);
-  const uint64_t ok = ((uint64_t)hi << 32) | lo;
-  if (beats(ok, oid, k, id)) {
-    k = ok;
-    id = oid;
-  }
-}
-
 __device__ __forceinline__ uint32_t rdlane(uint32_t v, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
 }
 
-// Softmax mode: key and id packed into one u64, (ord(key) << 32) | ~id, so
-// that "better" is plain unsigned order.  Wave max: 4 in-row DPP exchanges,
-// then row_bcast15 (rows 1, 3 take lane 15 of the row before) and row_bcast31
-// (rows 2, 3 take lane 31): lane 63 ends with the wave's maximum.
 template <int CTRL, int ROWS>
-__device__ __forceinline__ void dpp_max_u64(uint64_t& v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v,
-                                                            CTRL, ROWS, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(
-      (int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xF, false);
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
-  v = o > v ? o : v;
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROWS, 0xF, false);
+  return o > v ? o : v;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  dpp_max_u64<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  dpp_max_u64<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  dpp_max_u64<0x141, 0xF>(v);  // row_half_mirror
-  dpp_max_u64<0x140, 0xF>(v);  // row_mirror
-  dpp_max_u64<0x142, 0xA>(v);  // row_bcast15
-  dpp_max_u64<0x143, 0xC>(v);  // row_bcast31
-  return ((uint64_t)rdlane((uint32_t)(v >> 32), 63) << 32) | rdlane((uint32_t)v, 63);
+// Maximum of v over the wave (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast15: rows 1, 3 take lane 15 of the row before
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast31: rows 2, 3 take lane 31
+  return rdlane(v, 63);
+}
+
+// Sum of v over the wave: butterfly inside 16-lane rows (DPP), then the four
+// row sums as (r0 + r1) + (r2 + r3).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  auto step = [&](auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)u, (int)(uint32_t)u, C, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(u >> 32),
+                                                              (int)(uint32_t)(u >> 32), C, 0xF, 0xF, false);
+    v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  };
+  step(std::integral_constant<int, 0xB1>{});
+  step(std::integral_constant<int, 0x4E>{});
+  step(std::integral_constant<int, 0x141>{});
+  step(std::integral_constant<int, 0x140>{});
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  double r[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    r[q] = __longlong_as_double(
+        (long long)(((uint64_t)rdlane((uint32_t)(u >> 32), 16 * q) << 32) | rdlane((uint32_t)u, 16 * q)));
+  return (r[0] + r[1]) + (r[2] + r[3]);
 }
 
 // Top-k of one token.  L[i] = logit of expert lane + 64 i (ignored past E).
-// Writes ids[0..k) and weights[0..k) of the token.
-template <int MODE>
+// Writes ids[0..k) and weights[0..k) of the token; returns this lane's
+// selected expert for lanes < k.
+template <int MODE, int NSL>
 __device__ __forceinline__ uint32_t gate_token(const float (&L)[4], const float* __restrict__ bias,
-                                           int E, int k, float routed_scale, float eps,
-                                           int32_t* __restrict__ ids_row,
-                                           float* __restrict__ w_row) {
+                                               int E, int k, float routed_scale, float eps,
+                                               int32_t* __restrict__ ids_row,
+                                               float* __restrict__ w_row) {
   const int lane = threadIdx.x & 63;
-  constexpr uint32_t NO_ID = 0xffffffffu;
-  uint64_t key[4];
-  uint32_t id[4];
-  double sval[4];
+  uint32_t khi[NSL], klo[NSL];  // 0 = retired or no expert (below every real key)
+  double sval[NSL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NSL; ++i) {
     const int e = lane + 64 * i;
-    key[i] = 0;  // below every real key, even -inf
-    id[i] = NO_ID;
+    khi[i] = 0;
+    klo[i] = 0;
     sval[i] = 0.0;
     if (e < E) {
-      id[i] = (uint32_t)e;
       if (MODE == 0) {
-        key[i] = ord_key32(bias ? (L[i] + bias[e]) : L[i]);  // fp32 add, as the oracle
+        khi[i] = ord_key32(bias ? (L[i] + bias[e]) : L[i]);  // fp32 add, as the oracle
       } else {
         const double sg = 1.0 / (1.0 + exp(-(double)L[i]));
         sval[i] = sg;
-        key[i] = ord_key64(bias ? sg + (double)bias[e] : sg);
+        const uint64_t o = ord_key64(bias ? sg + (double)bias[e] : sg);
+        khi[i] = (uint32_t)(o >> 32);
+        klo[i] = (uint32_t)o;
       }
     }
   }
-  uint64_t my_key = 0;
-  uint32_t my_id = 0;
-  if (MODE == 0) {
+  uint32_t my_key = 0, my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    uint32_t m = khi[0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) key[i] = key[i] ? ((key[i] << 32) | (NO_ID - id[i])) : 0;
-    for (int j = 0; j < k; ++j) {
-      uint64_t b = key[0];
+    for (int i = 1; i < NSL; ++i) m = max(m, khi[i]);
+    const uint32_t mh = wave_max_u32(m);
+    uint32_t ml = 0;
+    if (MODE == 1) {
+      uint32_t c = 0;
 #pragma unroll
-      for (int i = 1; i < 4; ++i) b = key[i] > b ? key[i] : b;
-      const uint64_t w = wave_max_u64(b);  // wave-uniform; keys are unique (ids differ)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) key[i] = key[i] == w ? 0 : key[i];
-      if (lane == j) {
-        my_key = w >> 32;
-        my_id = NO_ID - (uint32_t)w;
-      }
+      for (int i = 0; i < NSL; ++i)
+        if (khi[i] == mh) c = max(c, klo[i]);
+      ml = wave_max_u32(c);
     }
-  }
-  for (int j = 0; MODE == 1 && j < k; ++j) {
-    uint64_t bk = key[0];
-    uint32_t bi = id[0];
+    // smallest id holding the maximum: slot by slot, then the lowest lane
+    uint32_t wid = 0;
 #pragma unroll
-    for (int i = 1; i < 4; ++i)
-      if (beats(key[i], id[i], bk, bi)) {
-        bk = key[i];
-        bi = id[i];
-      }
-    dpp_keep_best<0xB1>(bk, bi);   // quad_perm [1,0,3,2]
-    dpp_keep_best<0x4E>(bk, bi);   // quad_perm [2,3,0,1]
-    dpp_keep_best<0x141>(bk, bi);  // row_half_mirror
-    dpp_keep_best<0x140>(bk, bi);  // row_mirror
-    uint64_t wk = ((uint64_t)rdlane((uint32_t)(bk >> 32), 0) << 32) | rdlane((uint32_t)bk, 0);
-    uint32_t wi = rdlane(bi, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-      const uint64_t rk =
-          ((uint64_t)rdlane((uint32_t)(bk >> 32), 16 * r) << 32) | rdlane((uint32_t)bk, 16 * r);
-      const uint32_t ri = rdlane(bi, 16 * r);
-      if (beats(rk, ri, wk, wi)) {
-        wk = rk;
-        wi = ri;
-      }
+    for (int i = NSL - 1; i >= 0; --i) {
+      const unsigned long long bal =
+          __ballot(khi[i] == mh && (MODE == 0 || klo[i] == ml) && (khi[i] | klo[i]) != 0);
+      if (bal) wid = 64u * i + (uint32_t)(__ffsll((long long)bal) - 1);
     }
-    // wi is wave-uniform; its owner retires it
+    // the owner retires it
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (id[i] == wi) {
-        key[i] = 0;
-        id[i] = NO_ID;
+    for (int i = 0; i < NSL; ++i)
+      if ((uint32_t)(lane + 64 * i) == wid) {
+        khi[i] = 0;
+        klo[i] = 0;
       }
     if (lane == j) {
-      my_key = wk;
-      my_id = wi;
+      my_key = mh;
+      my_id = wid;
     }
   }
   double v;
@@ -427,15 +407,13 @@ __device__ __forceinline__ uint32_t gate_token(const float (&L)[4], const float*
     const int src = (int)(my_id & 63u), slot = (int)(my_id >> 6);
     double sv = 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NSL; ++i) {
       const double o = __shfl(sval[i], src, 64);
       if (slot == i) sv = o;
     }
     v = (lane < k) ? sv : 0.0;
   }
-  double sum = v;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) sum += __shfl_xor(sum, d, 64);
+  const double sum = wave_sum_f64(v);
   if (lane < k) {
     double w;
     if (MODE == 0)
@@ -445,10 +423,10 @@ __device__ __forceinline__ uint32_t gate_token(const float (&L)[4], const float*
     ids_row[lane] = (int32_t)my_id;
     w_row[lane] = (float)w;
   }
-  return my_id;  // lanes < k: the expert of slot lane
+  return my_id;
 }
 
-template <int MODE>
+template <int MODE, int NSL>
 __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict__ logits,
                                                         const float* __restrict__ bias, int T,
                                                         int E, int k, float routed_scale,
@@ -463,7 +441,8 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
     const int e = lane + 64 * i;
     L[i] = e < E ? logits[(size_t)t * E + e] : 0.f;
   }
-  gate_token<MODE>(L, bias, E, k, routed_scale, eps, ids + (size_t)t * k, wout + (size_t)t * k);
+  gate_token<MODE, NSL>(L, bias, E, k, routed_scale, eps, ids + (size_t)t * k,
+                        wout + (size_t)t * k);
 }
 
 // --------------------------------------------------- S1+S2+S3/S4, decode ---
@@ -477,7 +456,7 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
 // across waves through per-wave counts in LDS; expert bases are the exclusive
 // scan of the counts.  The order (expert, then pair index) is the stable
 // counting sort of the standalone route kernels.
-template <int MODE>
+template <int MODE, int NSL>
 __global__ __launch_bounds__(1024) void gate_route_small(
     const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E, int k,
     float routed_scale, float eps, float* __restrict__ logits, int32_t* __restrict__ ids,
@@ -515,7 +494,7 @@ __global__ __launch_bounds__(1024) void gate_route_small(
       const int e = lane + 64 * i;
       if (e < E) logits[(size_t)wave * E + e] = L[i];
     }
-    const uint32_t my = gate_token<MODE>(L, bias, E, k, routed_scale, eps,
+    const uint32_t my = gate_token<MODE, NSL>(L, bias, E, k, routed_scale, eps,
                                          ids + (size_t)wave * k, wout + (size_t)wave * k);
     if (lane < k) sids[wave * k + lane] = (int)my;
   }
@@ -566,31 +545,57 @@ __global__ __launch_bounds__(1024) void gate_route_small(
   if (tid == 0 && dev_status != nullptr) *dev_status = bad ? 1 : 0;
 }
 
+// Slots per lane for E experts (lane l holds experts l + 64 i).
+template <template <int, int> class F, typename... A>
+static void by_mode_slots(int mode, int E, A... args) {
+  const int nsl = (E + 63) / 64;
+  if (mode == 0) {
+    if (nsl <= 1) F<0, 1>::run(args...);
+    else if (nsl == 2) F<0, 2>::run(args...);
+    else if (nsl == 3) F<0, 3>::run(args...);
+    else F<0, 4>::run(args...);
+  } else {
+    if (nsl <= 1) F<1, 1>::run(args...);
+    else if (nsl == 2) F<1, 2>::run(args...);
+    else if (nsl == 3) F<1, 3>::run(args...);
+    else F<1, 4>::run(args...);
+  }
+}
+
+template <int MODE, int NSL>
+struct GateRouteSmall {
+  static void run(hipStream_t s, const float* partial, int S, const float* bias, int T, int E, int k,
+                  float routed_scale, float eps, float* logits, int32_t* ids, float* w,
+                  int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                  int32_t* dev_status) {
+    hipLaunchKernelGGL((gate_route_small<MODE, NSL>), dim3(1), dim3(1024), 0, s, partial, S, bias,
+                       T, E, k, routed_scale, eps, logits, ids, w, counts, offsets, sorted_pair,
+                       pair_pos, dev_status);
+  }
+};
+
+template <int MODE, int NSL>
+struct GateTopk {
+  static void run(hipStream_t s, const float* logits, const float* bias, int T, int E, int k,
+                  float routed_scale, float eps, int32_t* ids, float* w) {
+    hipLaunchKernelGGL((gate_topk_kernel<MODE, NSL>), dim3((T + 3) / 4), dim3(256), 0, s, logits,
+                       bias, T, E, k, routed_scale, eps, ids, w);
+  }
+};
+
 int launch_gate_route_small(const float* partial, int H, const float* bias, int T, int E, int k,
                             int mode, float routed_scale, float eps, float* logits, int32_t* ids,
                             float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                             int32_t* pair_pos, int32_t* dev_status, hipStream_t s) {
-  const int S = H / RP_HS;
-  if (mode == 0)
-    hipLaunchKernelGGL(gate_route_small<0>, dim3(1), dim3(1024), 0, s, partial, S, bias, T, E, k,
-                       routed_scale, eps, logits, ids, w, counts, offsets, sorted_pair, pair_pos,
-                       dev_status);
-  else
-    hipLaunchKernelGGL(gate_route_small<1>, dim3(1), dim3(1024), 0, s, partial, S, bias, T, E, k,
-                       routed_scale, eps, logits, ids, w, counts, offsets, sorted_pair, pair_pos,
-                       dev_status);
+  by_mode_slots<GateRouteSmall>(mode, E, s, partial, H / RP_HS, bias, T, E, k, routed_scale, eps,
+                                logits, ids, w, counts, offsets, sorted_pair, pair_pos,
+                                dev_status);
   return launch_status();
 }
 
 int launch_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,
                      float routed_scale, float eps, int32_t* ids, float* w, hipStream_t s) {
-  const dim3 grid((T + 3) / 4), block(256);
-  if (mode == 0)
-    hipLaunchKernelGGL(gate_topk_kernel<0>, grid, block, 0, s, logits, bias, T, E, k,
-                       routed_scale, eps, ids, w);
-  else
-    hipLaunchKernelGGL(gate_topk_kernel<1>, grid, block, 0, s, logits, bias, T, E, k,
-                       routed_scale, eps, ids, w);
+  by_mode_slots<GateTopk>(mode, E, s, logits, bias, T, E, k, routed_scale, eps, ids, w);
   return launch_status();
 }
 
