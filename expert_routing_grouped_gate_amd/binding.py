@@ -345,10 +345,11 @@ class MoeLayer:
         self._T = T
         return b
 
-    def time_ffn_up(self, begin: Optional[torch.cuda.Event], end: Optional[torch.cuda.Event]):
-        """Have later forward calls record these events (created by torch,
-        already recorded once so that their handles exist) around the
-        grouped GEMM1 launch; None, None to stop."""
+    def time_ffn_up(self, begin, end):
+        """Have later forward calls record these events around the grouped
+        GEMM1 launch: objects whose `cuda_event` is a hipEvent_t handle (a
+        torch.cuda.Event recorded once, or a raw HIP event); None, None to
+        stop."""
         assert self._T is not None, "call alloc() or forward() first"
         self.cbuf.ev_ffn_up_begin = None if begin is None else begin.cuda_event
         self.cbuf.ev_ffn_up_end = None if end is None else end.cuda_event
