@@ -56,9 +56,23 @@ __device__ __forceinline__ void split3_bf16(const float* w8, u32x4& hi, u32x4& m
 // path needs no separate quantiser launch.
 constexpr int RP_HS = 256;
 
+// Many tokens: the MFMA router splits K over ks blocks per output tile when
+// the tiles alone would leave CUs idle (about 2048 blocks in flight), ks a
+// power of two dividing the H/32 K-steps; the ks partial tiles are summed in
+// order by router_reduce.
+constexpr int RM_TT = 32, RM_TE = 64;
+
+static int router_ksplit(int T, int H, int E) {
+  const long long tiles = (long long)((T + RM_TT - 1) / RM_TT) * ((E + RM_TE - 1) / RM_TE);
+  int ks = 1;
+  while (ks < 8 && tiles * ks * 2 <= 2048 && (H / 32) % (ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
 size_t router_workspace_bytes(int T, int H, int E) {
-  if (T > 64) return 0;
-  return (size_t)(H / RP_HS) * (size_t)T * (size_t)E * sizeof(float);
+  if (T <= 64) return (size_t)(H / RP_HS) * (size_t)T * (size_t)E * sizeof(float);
+  const int ks = router_ksplit(T, H, E);
+  return ks > 1 ? (size_t)ks * (size_t)T * (size_t)E * sizeof(float) : 0;
 }
 
 __global__ __launch_bounds__(64) void router_partial(const uint16_t* __restrict__ x,
@@ -167,8 +181,8 @@ __global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ p
 // Many tokens (prefill): block tile 32 tokens x 64 experts, K step 32,
 // operands staged in double-buffered LDS (the split is done once, by the
 // loading thread); wave w owns experts 16w..16w+15 of the tile and both
-// 16-token halves (6 MFMAs per K step).
-constexpr int RM_TT = 32, RM_TE = 64;
+// 16-token halves (6 MFMAs per K step).  Block z of gridDim.z covers the
+// z-th 1/gridDim.z of K and writes its partial tile to logits + z*T*E.
 
 __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wr, int T,
@@ -179,10 +193,12 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * RM_TT, e0 = blockIdx.y * RM_TE;
+  const int nk = H / 32 / (int)gridDim.z, kbeg = (int)blockIdx.z * nk * 32;
+  logits += (size_t)blockIdx.z * T * E;
   // loaders: threads 0..127 -> x (token tid/4, chunk tid%4); all -> wr (expert tid/4, chunk tid%4)
   const int lrow = tid >> 2, lch = tid & 3;
-  const uint16_t* xp = x + (size_t)min(t0 + (lrow & 31), T - 1) * H + lch * 8;
-  const float* wp = wr + (size_t)min(e0 + lrow, E - 1) * H + lch * 8;
+  const uint16_t* xp = x + (size_t)min(t0 + (lrow & 31), T - 1) * H + kbeg + lch * 8;
+  const float* wp = wr + (size_t)min(e0 + lrow, E - 1) * H + kbeg + lch * 8;
   // two register sets: step k+2 is loaded while step k computes and step k+1
   // waits to be split and stored into the other LDS buffer
   u32x4 rx0, rx1;
@@ -214,7 +230,6 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
       acc1 = mfma16x16x32(a1, b, acc1);
     }
   };
-  const int nk = H / 32;
   gload(rx0, rw0, 0);
   if (nk > 1) gload(rx1, rw1, 32);
   lstore(rx0, rw0, 0);
@@ -256,8 +271,13 @@ int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E
     hipLaunchKernelGGL(router_reduce, dim3((T * E + 255) / 256), dim3(256), 0, s, ws, H / RP_HS,
                        T, E, logits);
   } else {
-    hipLaunchKernelGGL(router_logits_mfma, dim3((T + RM_TT - 1) / RM_TT, (E + RM_TE - 1) / RM_TE),
-                       dim3(256), 0, s, x, wr, T, H, E, logits);
+    const int ks = router_ksplit(T, H, E);
+    hipLaunchKernelGGL(router_logits_mfma,
+                       dim3((T + RM_TT - 1) / RM_TT, (E + RM_TE - 1) / RM_TE, ks), dim3(256), 0, s,
+                       x, wr, T, H, E, ks > 1 ? ws : logits);
+    if (ks > 1)
+      hipLaunchKernelGGL(router_reduce, dim3((T * E + 255) / 256), dim3(256), 0, s, ws, ks, T, E,
+                         logits);
   }
   return launch_status();
 }

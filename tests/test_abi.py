@@ -59,7 +59,11 @@ def test_router_logits_checks(lib):
     ws = lib.moe_router_workspace_size(4, 256, 8)
     assert ws == 1 * 4 * 8 * 4                                   # one 256-wide slice of partials
     assert lib.moe_router_workspace_size(4, 4096, 128) == 16 * 4 * 128 * 4
-    assert lib.moe_router_workspace_size(65, 4096, 128) == 0    # many tokens: no partials
+    # many tokens: K split over 8 blocks per 32x64 tile while that keeps <= 2048 blocks
+    assert lib.moe_router_workspace_size(65, 4096, 128) == 8 * 65 * 128 * 4
+    assert lib.moe_router_workspace_size(4096, 4096, 128) == 8 * 4096 * 128 * 4
+    assert lib.moe_router_workspace_size(4096, 4096, 192) == 4 * 4096 * 192 * 4
+    assert lib.moe_router_workspace_size(65536, 4096, 256) == 0     # enough tiles: no split
     assert f(None, FAKE, 4, 256, 8, FAKE, FAKE, ws, None) == NULL
     assert f(FAKE, FAKE, 4, 255, 8, FAKE, FAKE, ws, None) == UNSUP        # H % 256
     assert f(FAKE, FAKE, 4, 256, 257, FAKE, FAKE, ws, None) == UNSUP      # E > 256
@@ -130,7 +134,7 @@ def test_layer_forward_checks(lib):
     assert f(ctypes.byref(d2), FAKE, 4, FAKE, ctypes.byref(b), None) == SHAPE  # H mismatch
     # 16 tokens: the router's partial sums (1 slice x 16 x 8 fp32)
     assert lib.moe_layer_workspace_size(ctypes.byref(d), 16) == 16 * 8 * 4
-    assert lib.moe_layer_workspace_size(ctypes.byref(d), 100) == 0
+    assert lib.moe_layer_workspace_size(ctypes.byref(d), 100) == 8 * 100 * 8 * 4  # split-K router
 
 
 def test_mx_pack_checks_and_sizes(lib):
