@@ -31,7 +31,7 @@
 
 namespace moe {
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 
 // ------------------------------------------------------------ S0 quant ---
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ x, int rows,
@@ -137,29 +137,6 @@ int launch_mx_pack(const uint8_t* codes, const uint8_t* scales, int G, int R, in
   return launch_status();
 }
 
-// -------------------------------------------------------- scaled MFMA -----
-__device__ __forceinline__ f32x4 mfma_fp4_fp8(u32x4 a_fp4, i32x8 b_fp8, uint32_t sa, uint32_t sb,
-                                              f32x4 c) {
-  i32x8 a;
-  a[0] = (int)a_fp4[0];
-  a[1] = (int)a_fp4[1];
-  a[2] = (int)a_fp4[2];
-  a[3] = (int)a_fp4[3];
-  a[4] = a[5] = a[6] = a[7] = 0;
-  // A format 4 = E2M1, B format 0 = E4M3; scale byte 0 of each scale operand
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b_fp8, c, 4, 0, 0, (int)sa, 0, (int)sb);
-}
-
-// E4M3 operand of one lane: 16 bytes at p (k = 16g..) and 16 bytes at p + 64
-// (k = 64 + 16g..), where p = row + k0 + 16g.
-__device__ __forceinline__ i32x8 ld32_fp8(const uint8_t* p) {
-  const u32x4 lo = ld16(p), hi = ld16(p + 64);
-  i32x8 r;
-  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
-  r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
-  return r;
-}
-
 // ------------------------------------------------ streaming W4A8 GEMMs ---
 // One wave owns a whole tile (16 activation rows x 4 groups of 16 weight
 // rows, the full K) and walks its tiles as one sequence of U-step batches,
@@ -210,13 +187,6 @@ template <bool SWIGLU>
 __device__ __forceinline__ int mx_wrow0(const GroupedGemm& g, int n0, int j) {
   if (SWIGLU) return (j >= 2 ? g.up_off : 0) + n0 + 16 * (j & 1);
   return n0 + 16 * j;
-}
-
-// Raw buffer descriptor over [p, p + bytes): loads address it as a uniform
-// base (scalar registers) plus a 32-bit lane offset and a scalar offset.
-// Word 3 = 0x00020000: the raw (untyped, stride 0) dword format on gfx9.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
 // Batch of U K-steps (128 each) starting at step st0 of tile t.  The weights

@@ -79,6 +79,10 @@ CONFIGS = {
     "qwen3_decode_w4a8": LayerConfig("qwen3_decode_w4a8", T=16, H=4096, E=128, k=8, I=1536,
                                      bias="zipf1.1", fmt="w4a8",
                                      family_seed=1005, x_seed=5),
+    # the prefill shape with MXFP4 weights and MXFP8 activations (same weights
+    # as the W4A8 decode layer, no router bias)
+    "qwen3_prefill_w4a8": LayerConfig("qwen3_prefill_w4a8", T=4096, H=4096, E=128, k=8, I=1536,
+                                      fmt="w4a8", family_seed=1005, x_seed=6),
 }
 
 
