@@ -252,7 +252,7 @@ int moe_grouped_ffn_up(const MoeFfnWeights* w, const void* x, const uint8_t* x_s
   if (mx) {
     g.w_gstride = (long long)w->I * w->H;  // bytes: 2I rows of H/2
     g.ws_gstride = (long long)moe::mx_packed_scales_bytes(2 * w->I, w->H);
-    return moe::launch_ffn_up_w4a8(g, as_stream(stream));
+    return moe::launch_ffn_up_w4a8(g, small_m((long long)T * k, w->E), as_stream(stream));
   }
   g.w_gstride = 2ll * w->I * w->H;
   return moe::launch_ffn_up_bf16(g, small_m((long long)T * k, w->E), as_stream(stream));
@@ -281,7 +281,7 @@ int moe_grouped_ffn_down(const MoeFfnWeights* w, const void* act, const uint8_t*
   if (mx) {
     g.w_gstride = (long long)w->H * (w->I / 2);
     g.ws_gstride = (long long)moe::mx_packed_scales_bytes(w->H, w->I);
-    return moe::launch_ffn_down_w4a8(g, as_stream(stream));
+    return moe::launch_ffn_down_w4a8(g, small_m((long long)T * k, w->E), as_stream(stream));
   }
   g.w_gstride = (long long)w->H * w->I;
   return moe::launch_ffn_down_bf16(g, small_m((long long)T * k, w->E), as_stream(stream));
@@ -316,7 +316,7 @@ int moe_shared_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scale
   g.out = shared_act;
   g.out_scales = shared_act_scales;
   const bool sm = T <= 16;
-  st = mx ? moe::launch_ffn_up_w4a8(g, as_stream(stream)) : moe::launch_ffn_up_bf16(g, sm, as_stream(stream));
+  st = mx ? moe::launch_ffn_up_w4a8(g, sm, as_stream(stream)) : moe::launch_ffn_up_bf16(g, sm, as_stream(stream));
   if (st) return st;
   GroupedGemm d = g;
   d.A = shared_act;
@@ -328,7 +328,7 @@ int moe_shared_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scale
   d.up_off = 0;
   d.out = shared_y;
   d.out_scales = nullptr;
-  return mx ? moe::launch_ffn_down_w4a8(d, as_stream(stream)) : moe::launch_ffn_down_bf16(d, sm, as_stream(stream));
+  return mx ? moe::launch_ffn_down_w4a8(d, sm, as_stream(stream)) : moe::launch_ffn_down_bf16(d, sm, as_stream(stream));
 }
 
 int moe_grouped_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales, int T, int k,

@@ -57,6 +57,42 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   return xcd * base + (xcd < rem ? xcd : rem) + local;
 }
 
+// Explicit waits and barriers of the LDS-staged GEMMs (DMA ring + MFMA).
+// s_waitcnt lgkmcnt(n) only (vmcnt and expcnt left open; gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
+}
+
+// s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt left open (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// s_waitcnt vmcnt(n) only (lgkmcnt and expcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Make the compiler treat these registers as read here, so that it waits
+// for their pending LDS loads at this point (its own, tracked wait).
+template <int N>
+__device__ __forceinline__ void use_regs(const u32x4* r) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(r[i]));
+}
+
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Activation row of sorted row r: the token of pair sorted_pair[r] when
 // gathering (clamped into [0, rows/topk)), else r itself.
 __device__ __forceinline__ int gather_row(const int32_t* __restrict__ sorted_pair, int gather,

@@ -162,41 +162,6 @@ struct Tiled {
   static_assert(BM * (BNOUT + 8) * 2 <= NSTAGE * STAGE * 16, "epilogue tile fits");
 };
 
-// s_waitcnt lgkmcnt(n) only (vmcnt and expcnt left open; gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_lgkm() {
-  static_assert(N >= 0 && N < 16, "lgkmcnt range");
-  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
-}
-
-// s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt left open (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-
-// s_waitcnt vmcnt(n) only (lgkmcnt and expcnt left open).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Make the compiler treat these registers as read here, so that it waits
-// for their pending LDS loads at this point (its own, tracked wait).
-template <int N>
-__device__ __forceinline__ void use_regs(const u32x4* r) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(r[i]));
-}
-
-__device__ __forceinline__ void block_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // One output tile.  LDS holds NSTAGE stages of [A rows 0..BM-1 | B rows
 // BM..BM+BN-1] x 8 chunks of 16 B (one K step of 64), chunk c of row r stored
 // at c ^ (r & 7).  Stages are filled by global_load_lds_dwordx4: each wave

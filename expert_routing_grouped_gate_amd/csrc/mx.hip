@@ -351,10 +351,13 @@ static void launch_mx_stream(const GroupedGemm& g, hipStream_t s) {
   hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, g, nt);
 }
 
-// K = H (a multiple of 256): batches of 2 K-steps.
-int launch_ffn_up_w4a8(const GroupedGemm& g, hipStream_t s) {
+// K = H (a multiple of 256): batches of 2 K-steps.  Many rows per expert
+// (small_m false) and whole tiles: the LDS-tiled kernel (mx_tiled.hip).
+int launch_ffn_up_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (!mx_matrix_fits(g, true)) return -3;  // MOE_ERR_UNSUPPORTED
-  if ((g.K / 128) % 2 == 0)
+  if (!small_m && mx_tiled_fits(g, true))
+    launch_mx_tiled(g, true, s);
+  else if ((g.K / 128) % 2 == 0)
     launch_mx_stream<true, 2>(g, s);
   else
     launch_mx_stream<true, 1>(g, s);
@@ -362,9 +365,11 @@ int launch_ffn_up_w4a8(const GroupedGemm& g, hipStream_t s) {
 }
 
 // K = I (a multiple of 128); N = H (a multiple of 64).
-int launch_ffn_down_w4a8(const GroupedGemm& g, hipStream_t s) {
+int launch_ffn_down_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (!mx_matrix_fits(g, false)) return -3;  // MOE_ERR_UNSUPPORTED
-  if ((g.K / 128) % 2 == 0)
+  if (!small_m && mx_tiled_fits(g, false))
+    launch_mx_tiled(g, false, s);
+  else if ((g.K / 128) % 2 == 0)
     launch_mx_stream<false, 2>(g, s);
   else
     launch_mx_stream<false, 1>(g, s);

@@ -27,6 +27,16 @@ SMALL = {
     # Hy3-style gate with an always-on W4A8 shared expert
     "mx_shared": CFG["hy3"].with_(name="mx_shared", T=40, H=512, E=16, k=4, I=256, shared_I=384,
                                   fmt="w4a8", family_seed=1108, x_seed=25),
+    # more than 16 rows per expert and K a multiple of 512: the LDS-tiled
+    # kernels; one quad of K-steps per tile (the peeled last quad only) ...
+    "mx_tiled": CFG["qwen3_decode_w4a8"].with_(name="mx_tiled", T=512, H=512, E=8, k=2, I=512,
+                                               family_seed=1109, x_seed=26),
+    # ... several quads, ragged 128-row m-tiles, 8 n-tiles in each GEMM
+    "mx_tiled_deep": CFG["qwen3_decode_w4a8"].with_(name="mx_tiled_deep", T=300, H=2048, E=4, k=2,
+                                                    I=1024, family_seed=1110, x_seed=27),
+    # shared expert (one identity group of T rows) on the tiled kernels too
+    "mx_tiled_shared": CFG["hy3"].with_(name="mx_tiled_shared", T=200, H=1024, E=8, k=4, I=512,
+                                        shared_I=512, fmt="w4a8", family_seed=1111, x_seed=28),
 }
 
 
@@ -60,16 +70,32 @@ def _quant_codes_close(gpu_codes, gpu_scales, ref_vals, what):
     sit next to a rounding boundary).  The value quantised is SiLU(g) * u of
     two fp32 dot products over K, whose rounding error is absolute: relative
     to the largest value of its 32-block, about 2^-14 covers it, so elements
-    that cancel to almost zero are held to that instead of one E4M3 step."""
-    gv = mx.mxfp8_dequant(gpu_codes, gpu_scales)
+    that cancel to almost zero are held to that instead of one E4M3 step.
+
+    The block exponent is an integer decided by the block's amax, which the
+    GPU takes from its fp32 values: a block whose exact amax lies within
+    2^-12 (relative) of the power of two between two exponents may take the
+    other one.  Such blocks (and only such) may differ by one in the scale;
+    every block's codes are compared with the exact values quantised with the
+    GPU's exponent (the oracle's own codes wherever the exponents agree)."""
+    rows, cols = ref_vals.shape
     rc, rs = mx.mxfp8_quantize(ref_vals)
-    rv = mx.mxfp8_dequant(rc, rs)
+    gs, rsi = gpu_scales.astype(np.int64), rs.astype(np.int64)
+    amax_b = np.abs(ref_vals).reshape(rows, cols // 32, 32).max(-1)
+    flip = gs != rsi
+    if flip.any():
+        edge = 2.0 ** (np.maximum(gs, rsi)[flip] - 127 + 8)   # amax where the exponent steps
+        near = np.abs(amax_b[flip] / edge - 1.0) <= 2.0 ** -12
+        assert np.all((np.abs(gs - rsi)[flip] == 1) & near), f"{what}: block scales differ"
+    scale = np.repeat(mx.e8m0_decode(gpu_scales), 32, -1)
+    rq = mx.e4m3_encode_rne(ref_vals / scale)
+    rv = mx.e4m3_decode(rq) * scale
+    gv = mx.mxfp8_dequant(gpu_codes, gpu_scales)
     same = gv == rv
     assert same.mean() > 0.995, f"{what}: only {same.mean():.4f} of codes equal"
     d = np.abs(gv - rv)
-    rows, cols = rv.shape
-    amax = np.repeat(np.abs(ref_vals).reshape(rows, cols // 32, 32).max(-1), 32, -1)
-    step = np.abs(rv) * 0.126 + np.repeat(mx.e8m0_decode(rs), 32, -1) * 2.0 ** -9 * 1.01
+    amax = np.repeat(amax_b, 32, -1)
+    step = np.abs(rv) * 0.126 + scale * 2.0 ** -9 * 1.01
     assert np.all(d <= np.maximum(step, amax * 2.0 ** -14)), what
 
 
@@ -155,6 +181,37 @@ def test_mx_layer_small(name):
 
 def test_mx_layer_full_decode():
     _layer_check(CFG["qwen3_decode_w4a8"])
+
+
+def test_mx_layer_full_prefill():
+    # 4096 tokens (tiled GEMMs): values on a sample of tokens
+    _layer_check(CFG["qwen3_prefill_w4a8"], tokens=[0, 1, 2, 777, 2048, 4094, 4095])
+
+
+@pytest.mark.parametrize("name", ["mx_tiled", "mx_tiled_deep"])
+def test_mx_tiled_equals_streaming_bit_for_bit(name):
+    """A row's GEMM outputs depend only on that row, and both GEMM kernels
+    run the same scaled MFMAs over the same K-steps in the same order.  With
+    the routing of all T tokens, the first 16*E/k tokens alone (16 rows per
+    expert: streaming kernels) and all T tokens (tiled kernels) give the same
+    bits in every row of those tokens, in both GEMMs."""
+    L = get_layer(SMALL[name])
+    cfg = L.cfg
+    x = L.dev["x"]
+    xq, xs = B.mx_quantize(x)
+    logits = B.router_logits(x, L.dev["wr"])
+    ids, _ = B.gate_topk(logits, cfg.k, L.mode, L.dev["bias"], cfg.routed_scale, cfg.eps)
+    nfew = 16 * cfg.E // cfg.k
+    outs = []
+    for T in (nfew, cfg.T):
+        _, offsets, sp, pp = B.route(ids[:T].contiguous(), cfg.E)
+        act, act_s = B.grouped_ffn_up(L.weights, xq[:T], xs[:T], cfg.k, sp, offsets)
+        y = B.grouped_ffn_down(L.weights, act, act_s, T, cfg.k, offsets)
+        rows = pp[: nfew * cfg.k].long()          # rows of the first nfew tokens' pairs
+        outs.append((act[rows], act_s[rows], y[rows]))
+    torch.cuda.synchronize()
+    for few, many, what in zip(outs[0], outs[1], ("act codes", "act scales", "y")):
+        assert torch.equal(few, many), what
 
 
 def test_mx_layer_deterministic_and_graph_capture():
