@@ -250,8 +250,8 @@ __device__ __forceinline__ void mx_store(const GroupedGemm& g, const MxTile& t, 
     float a[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      a[i] = (acc[0][i] / (1.f + expf(-acc[0][i]))) * acc[2][i];
-      a[4 + i] = (acc[1][i] / (1.f + expf(-acc[1][i]))) * acc[3][i];
+      a[i] = silu_fast(acc[0][i]) * acc[2][i];
+      a[4 + i] = silu_fast(acc[1][i]) * acc[3][i];
     }
     float amax = 0.f;
 #pragma unroll

@@ -221,7 +221,6 @@ __device__ __forceinline__ void mx_tiled_tile(const GroupedGemm& g, uint8_t* sme
       if (u == 0) load_scales(as_nxt, ws_nxt, c_cur + 1);
     }
     if (!last || u < 3) read_frags(f ^ 1, (u + 1) & 3);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
       const uint32_t xsc = (as_cur[mi] >> (8 * u)) & 0xffu;
@@ -229,6 +228,24 @@ __device__ __forceinline__ void mx_tiled_tile(const GroupedGemm& g, uint8_t* sme
       for (int ni = 0; ni < NT; ++ni)
         acc[mi][ni] = mfma_fp4_fp8(wf[f][ni], af[f][mi], (ws_cur[ni] >> (8 * u)) & 0xffu, xsc,
                                    acc[mi][ni]);
+    }
+    // Issue order: one MFMA, then one of the step's global loads (DMA, and
+    // the scale loads at the start of a quad), then one MFMA and two LDS
+    // reads, and so on: with one wave per SIMD the memory instructions issue
+    // while the matrix core works instead of before it.
+    if (!last) {
+#pragma unroll
+      for (int i = 0; i < C::LPW + (u == 0 ? MT + NT : 0); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+      }
+    }
+    if (!last || u < 3) {
+#pragma unroll
+      for (int i = 0; i < (2 * MT + NT) / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS read
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -284,8 +301,8 @@ __device__ __forceinline__ void mx_tiled_tile(const GroupedGemm& g, uint8_t* sme
         float a[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          a[i] = (g0[i] / (1.f + expf(-g0[i]))) * u0[i];
-          a[4 + i] = (g1[i] / (1.f + expf(-g1[i]))) * u1[i];
+          a[i] = silu_fast(g0[i]) * u0[i];
+          a[4 + i] = silu_fast(g1[i]) * u1[i];
         }
         float amax = 0.f;
 #pragma unroll

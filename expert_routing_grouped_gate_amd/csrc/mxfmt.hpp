@@ -14,25 +14,27 @@ namespace moe {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // E4M3FN code of v (already divided by its block scale), RNE, saturating.
+// Branch-free: both the subnormal code (grid 2^-9 below 2^-6) and the normal
+// code are formed and one is selected.  Normal: E = floor(log2 a) in [-6, 8],
+// m = rint(a * 2^(3-E)) in [8, 16]; code = ((E + 7) << 3) + (m - 8), where
+// m = 16 carries into the exponent field by itself.  |v| >= 448 and NaN give
+// +-448 (0x7e); a value rounding to zero keeps its sign bit.
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
   const uint32_t bits = __float_as_uint(v);
   const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = __uint_as_float(bits & 0x7fffffffu);
-  if (!(a < 448.f)) return sign | 0x7eu;  // saturate (also catches NaN)
-  if (a < 0.015625f) {                    // below 2^-6: subnormal grid 2^-9
-    const uint32_t m = (uint32_t)rintf(a * 512.f);  // 0..8; 8 is 2^-6 = code 0x08
-    return sign | m;
-  }
-  int E = (int)((bits >> 23) & 0xffu) - 127;  // floor(log2 a), -6..8
-  const float q = __uint_as_float((uint32_t)(127 + 3 - E) << 23) * a;  // a * 2^(3-E) in [8,16)
-  uint32_t m = (uint32_t)rintf(q);
-  if (m == 16u) {
-    m = 8u;
-    ++E;
-  }
-  uint32_t code = ((uint32_t)(E + 7) << 3) | (m - 8u);
-  if (code > 0x7eu) code = 0x7eu;
-  return sign | code;
+  const float a = fminf(__uint_as_float(bits & 0x7fffffffu), 448.f);  // (fminf(NaN, 448) = 448)
+  const uint32_t sub = (uint32_t)rintf(a * 512.f);                     // 0..8 (8 = 2^-6 = code 0x08)
+  const int E = max((int)(__float_as_uint(a) >> 23) - 127, -6);
+  const float q = __uint_as_float((uint32_t)(127 + 3 - E) << 23) * a;  // a * 2^(3-E)
+  const uint32_t code = min(((uint32_t)(E + 7) << 3) + ((uint32_t)rintf(q) - 8u), 0x7eu);
+  return sign | (a < 0.015625f ? sub : code);
+}
+
+// SiLU(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (about one
+// ulp each; the result is then quantised to E4M3, whose step is 2^-3
+// relative).  Large negative g: e^-g overflows to inf and the result is -0.
+__device__ __forceinline__ float silu_fast(float g) {
+  return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
 }
 
 // floor(log2(amax)) - 8, clamped to [-127, 127]; amax zero or subnormal -> -127.
