@@ -140,12 +140,8 @@ __global__ __launch_bounds__(64) void router_partial(const uint16_t* __restrict_
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
       const int ex = mx_exponent(amax);
       const float inv = exp2_neg(ex);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo |= e4m3_encode(f[i] * inv) << (8 * i);
-        hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
-      }
+      const uint32_t lo = e4m3_pack4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+      const uint32_t hi = e4m3_pack4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
       if (t0 + fr < T) {
         const int col = h0 + 32 * st + 8 * fc;
         *reinterpret_cast<u32x2*>(xq + (size_t)(t0 + fr) * H + col) = u32x2{lo, hi};

@@ -12,7 +12,8 @@
 // e = floor(log2(amax)) - 8 clamped to [-127, 127] (amax 0 -> -127), scale
 // code e + 127, element = E4M3 round-to-nearest-even of v / 2^e saturated to
 // +-448; a value rounding to zero keeps its sign bit.  The encoder is
-// integer-exact (no hardware convert), so codes are reproducible bit for bit.
+// the hardware E4M3 convert after a +-448 clamp, equal to the rule on every
+// fp32 input, so codes are reproducible bit for bit.
 //
 // S0 (mx_quant): four lanes per 32-block, 8 elements per lane.
 // S5/S6 (ffn_mx_stream): weight-streaming grouped GEMMs on
@@ -55,11 +56,8 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   const int e = mx_exponent(amax);
   const float inv = exp2_neg(e);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= e4m3_encode(f[i] * inv) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= e4m3_encode(f[4 + i] * inv) << (8 * i);
+  const uint32_t lo = e4m3_pack4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+  const uint32_t hi = e4m3_pack4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
   if (ok) {
     *reinterpret_cast<u32x2*>(codes + c * 8) = u32x2{lo, hi};
     if ((threadIdx.x & 3) == 0) scales[c / 4] = (uint8_t)(e + 127);
@@ -260,12 +258,8 @@ __device__ __forceinline__ void mx_store(const GroupedGemm& g, const MxTile& t, 
     amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
     const int e = mx_exponent(amax);
     const float inv = exp2_neg(e);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= e4m3_encode(a[i] * inv) << (8 * i);
-      hi |= e4m3_encode(a[4 + i] * inv) << (8 * i);
-    }
+    const uint32_t lo = e4m3_pack4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+    const uint32_t hi = e4m3_pack4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv);
     if (li < t.nrows) {
       uint8_t* orow = static_cast<uint8_t*>(g.out) + (size_t)(t.row0 + li) * g.N;
       *reinterpret_cast<uint32_t*>(orow + t.n0 + 4 * kb) = lo;

@@ -311,12 +311,8 @@ __device__ __forceinline__ void mx_tiled_tile(const GroupedGemm& g, uint8_t* sme
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
         const int e = mx_exponent(amax);
         const float inv = exp2_neg(e);
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          lo |= e4m3_encode(a[i] * inv) << (8 * i);
-          hi |= e4m3_encode(a[4 + i] * inv) << (8 * i);
-        }
+        const uint32_t lo = e4m3_pack4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+        const uint32_t hi = e4m3_pack4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv);
         if (r < nrows) {
           const int col0 = n0 + 16 * (wn * (NT / 2) + 2 * b);
           uint8_t* orow = static_cast<uint8_t*>(g.out) + (size_t)(row0 + r) * g.N;

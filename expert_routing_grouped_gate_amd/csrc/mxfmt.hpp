@@ -3,8 +3,8 @@
 // and GEMM1's epilogue.  Block rule (32 consecutive elements): shared
 // exponent e = floor(log2(amax)) - 8 clamped to [-127, 127] (amax 0 -> -127),
 // element = E4M3FN round-to-nearest-even of v / 2^e saturated to +-448, a
-// value rounding to zero keeping its sign bit.  Integer-exact, no hardware
-// convert, so codes are reproducible bit for bit.
+// value rounding to zero keeping its sign bit.  Codes are a pure function of
+// the fp32 input (no data-dependent rounding state), reproducible bit for bit.
 #pragma once
 
 #include "common.hpp"
@@ -13,21 +13,20 @@ namespace moe {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// E4M3FN code of v (already divided by its block scale), RNE, saturating.
-// Branch-free: both the subnormal code (grid 2^-9 below 2^-6) and the normal
-// code are formed and one is selected.  Normal: E = floor(log2 a) in [-6, 8],
-// m = rint(a * 2^(3-E)) in [8, 16]; code = ((E + 7) << 3) + (m - 8), where
-// m = 16 carries into the exponent field by itself.  |v| >= 448 and NaN give
-// +-448 (0x7e); a value rounding to zero keeps its sign bit.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t bits = __float_as_uint(v);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = fminf(__uint_as_float(bits & 0x7fffffffu), 448.f);  // (fminf(NaN, 448) = 448)
-  const uint32_t sub = (uint32_t)rintf(a * 512.f);                     // 0..8 (8 = 2^-6 = code 0x08)
-  const int E = max((int)(__float_as_uint(a) >> 23) - 127, -6);
-  const float q = __uint_as_float((uint32_t)(127 + 3 - E) << 23) * a;  // a * 2^(3-E)
-  const uint32_t code = min(((uint32_t)(E + 7) << 3) + ((uint32_t)rintf(q) - 8u), 0x7eu);
-  return sign | (a < 0.015625f ? sub : code);
+// E4M3FN codes of four values already divided by their block scale: round
+// to nearest even, saturating at +-448, NaN to +-448 with its sign, a value
+// rounding to zero keeping its sign bit.  The hardware convert
+// (v_cvt_pk_fp8_f32, OCP E4M3FN on gfx950) rounds to nearest even and keeps
+// the sign of zero; clamping to +-448 first gives the saturation.  This equals
+// an integer implementation of the rule on every fp32 input (an exhaustive
+// check over all 2^32 bit patterns on gfx950).  Byte i = code of value i.
+__device__ __forceinline__ float e4m3_clamp(float v) {
+  return __builtin_isnan(v) ? __builtin_copysignf(448.f, v) : fminf(fmaxf(v, -448.f), 448.f);
+}
+
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), lo, true);
 }
 
 // SiLU(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (about one
