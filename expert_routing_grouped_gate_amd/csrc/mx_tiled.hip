@@ -74,74 +74,114 @@ __device__ __forceinline__ int mx_wave_block(int wn, int ni) {
   return wn * NT + ni;
 }
 
+// Per-tile state.  The ring streams across tiles: during the last quad of
+// K-steps of a tile, once stage u of the ring has been read by every wave, the
+// DMA of the next tile's step u goes into it, and the next tile's first scale
+// quad is loaded with its step 0; the row gathers of the next tile are issued
+// when the current tile starts.  A block's tile sequence is t, t + gridDim.x,
+// ... in the expert-major order (the m-tiles that share a weight tile are
+// neighbours; an expert's tiles stay on one XCD).
+struct MxTileInfo {
+  int grp, n0, row0, nrows;  // wave-uniform
+};
+
 template <bool SWIGLU, int WM, int WN, int NS>
-__device__ __forceinline__ void mx_tiled_tile(const GroupedGemm& g, uint8_t* smem, int n_tile,
-                                              int grp, int row0, int nrows) {
+__global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, int n_tiles) {
   using C = MxTiled<SWIGLU, WM, WN, NS>;
   constexpr int MT = C::MT, NT = C::NT;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE];
+  TileMap tm;
+  tm.init(g.offsets, g.G, g.ident_rows, C::BM, g.total_rows);
+  const int total = __builtin_amdgcn_readfirstlane(tm.total * n_tiles);
+  int t = blockIdx.x;
+  if (t >= total) return;  // uniform per block: no barrier is left waiting
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WM, wn = wave / WM;
   const int li = lane & 15, kb = lane >> 4;
-  const int K = g.K, ns = K / 128, nq = ns / 4;
-  const int n0 = n_tile * C::BNOUT;
+  const int K = g.K, ns = K / 128, nq = ns / 4;  // nq >= 2
   const uint8_t* A = static_cast<const uint8_t*>(g.A);
-  const uint8_t* Wg = static_cast<const uint8_t*>(g.W) + (size_t)grp * g.w_gstride;
-
-  // ---- DMA sources (per lane) -------------------------------------------
-  // activation group ra (8 rows): lane l fills row 8 ra + l/8, physical
-  // chunk l % 8, i.e. it loads logical chunk (l % 8) ^ (l / 8)
-  const uint8_t* asrc[C::LPA];
-#pragma unroll
-  for (int i = 0; i < C::LPA; ++i) {
-    const int row = 8 * (wave + C::NW * i) + (lane >> 3);
-    const int r = row0 + min(row, nrows - 1);  // rows past the tile end reuse a valid row
-    const int arow = gather_row(g.sorted_pair, g.gather, g.topk, g.total_rows, r);
-    asrc[i] = A + (size_t)arow * K + 16 * ((lane & 7) ^ (lane >> 3));
-  }
-  const uint8_t* wsrc[C::LPB];
-#pragma unroll
-  for (int i = 0; i < C::LPB; ++i) {
-    const int q = mx_block_row<SWIGLU, C::BN>(g, n0, wave + C::NW * i) / 16;
-    wsrc[i] = Wg + (size_t)q * ns * 1024 + lane * 16;
-  }
-  auto issue = [&](int buf, int st) {
-    uint8_t* stg = smem + buf * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::LPA; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(asrc[i] + st * 128),
-          (__attribute__((address_space(3))) void*)(stg + (wave + C::NW * i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::LPB; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(wsrc[i] + (size_t)st * 1024),
-          (__attribute__((address_space(3))) void*)(stg + C::ABYTES + (wave + C::NW * i) * 1024),
-          16, 0, 0);
-  };
-
-  // ---- scales (registers) ------------------------------------------------
   const int arows_total = g.gather ? g.total_rows / g.topk : g.total_rows;
   const __amdgpu_buffer_rsrc_t asr = mx_rsrc(g.A_scales, (uint32_t)arows_total * (uint32_t)(K / 32));
   const uint32_t wrows = SWIGLU ? 2u * (uint32_t)g.up_off : (uint32_t)g.N;
-  const __amdgpu_buffer_rsrc_t wsr =
-      mx_rsrc(g.W_scales + (size_t)grp * g.ws_gstride, wrows / 16u * (uint32_t)nq * 256u);
-  uint32_t aoff[MT];  // byte offset of this lane's activation scale row
+  const uint32_t wscale_bytes = wrows / 16u * (uint32_t)nq * 256u;
+
+  auto locate = [&](int tt) {
+    const int id = xcd_remap(tt, total);
+    int grp, first_mt, n_mt, grow0, grow1;
+    tm.find_group(id / n_tiles, grp, first_mt, n_mt, grow0, grow1);
+    const int local = id - first_mt * n_tiles;
+    const int n_tile = local / n_mt;
+    const int row0 = grow0 + (local - n_tile * n_mt) * C::BM;
+    MxTileInfo ti;
+    ti.grp = __builtin_amdgcn_readfirstlane(grp);
+    ti.n0 = __builtin_amdgcn_readfirstlane(n_tile * C::BNOUT);
+    ti.row0 = __builtin_amdgcn_readfirstlane(row0);
+    ti.nrows = __builtin_amdgcn_readfirstlane(min(C::BM, grow1 - row0));
+    return ti;
+  };
+  // Per-lane row offsets of a tile: adma[i] = byte offset in A of the 16
+  // bytes this lane's DMA i reads at step 0 (activation group ra = wave +
+  // NW i, 8 rows; lane l fills row 8 ra + l/8, physical chunk l % 8, i.e. it
+  // loads logical chunk (l % 8) ^ (l / 8)); aoff[mi] = byte offset of the
+  // scale row of this lane's activation row in fragment group mi.  Rows past
+  // the tile end reuse a valid row.
+  auto gather = [&](const MxTileInfo& ti, uint32_t* adma, uint32_t* aoff) {
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi) {
-    const int r = row0 + min(16 * (mi * WM + wm) + li, nrows - 1);
-    aoff[mi] = (uint32_t)gather_row(g.sorted_pair, g.gather, g.topk, g.total_rows, r) * (uint32_t)(K / 32);
-  }
-  int wq[NT];  // weight group (16-row block index) of group ni, wave-uniform
+    for (int i = 0; i < C::LPA; ++i) {
+      const int row = 8 * (wave + C::NW * i) + (lane >> 3);
+      const int r = ti.row0 + min(row, ti.nrows - 1);
+      const uint32_t arow = (uint32_t)gather_row(g.sorted_pair, g.gather, g.topk, g.total_rows, r);
+      adma[i] = arow * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+    }
 #pragma unroll
-  for (int ni = 0; ni < NT; ++ni)
-    wq[ni] = mx_block_row<SWIGLU, C::BN>(g, n0, mx_wave_block<SWIGLU, NT, C::BN>(wn, ni)) / 16;
+    for (int mi = 0; mi < MT; ++mi) {
+      const int r = ti.row0 + min(16 * (mi * WM + wm) + li, ti.nrows - 1);
+      aoff[mi] = (uint32_t)gather_row(g.sorted_pair, g.gather, g.topk, g.total_rows, r) *
+                 (uint32_t)(K / 32);
+    }
+  };
+  // DMA of step st of tile ti into stage buffer buf: LPA activation groups
+  // and LPB weight blocks of 1 KB per wave.
+  auto issue = [&](const MxTileInfo& ti, const uint32_t* adma, int buf, int st) {
+    uint8_t* stg = smem + buf * C::STAGE;
+    const uint8_t* Wg = static_cast<const uint8_t*>(g.W) + (size_t)ti.grp * g.w_gstride;
+#pragma unroll
+    for (int i = 0; i < C::LPA; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(A + (size_t)adma[i] + st * 128),
+          (__attribute__((address_space(3))) void*)(stg + (wave + C::NW * i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::LPB; ++i) {
+      const int q = mx_block_row<SWIGLU, C::BN>(g, ti.n0, wave + C::NW * i) / 16;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(Wg + (size_t)(q * ns + st) * 1024 + lane * 16),
+          (__attribute__((address_space(3))) void*)(stg + C::ABYTES + (wave + C::NW * i) * 1024),
+          16, 0, 0);
+    }
+  };
+
+  // ---- scales (registers) ------------------------------------------------
+  // Weight scales: the packed dword of group ni for a quad (byte u = step
+  // 4c + u).  Activation scales: 16 bytes per row per quad (word u = the four
+  // 32-blocks of step 4c + u), compacted to the byte of this lane's block kb.
   u32x4 as_nxt[MT];     // activation scales of the next quad, as loaded
   uint32_t as_cur[MT];  // byte u: this lane's 32-block (kb) at step 4c + u
   uint32_t ws_cur[NT], ws_nxt[NT];
-  // word u of the 16 bytes holds the four 32-blocks of step 4c + u
-  auto compact = [&]() {
+  auto load_scales = [&](const MxTileInfo& ti, const uint32_t* aoff, int c) {  // quad c
+    const __amdgpu_buffer_rsrc_t wsr = mx_rsrc(g.W_scales + (size_t)ti.grp * g.ws_gstride, wscale_bytes);
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) {
+      const int q = mx_block_row<SWIGLU, C::BN>(g, ti.n0, mx_wave_block<SWIGLU, NT, C::BN>(wn, ni)) / 16;
+      ws_nxt[ni] = __builtin_amdgcn_raw_buffer_load_b32(wsr, lane * 4, (q * nq + c) * 256, 0);
+    }
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+      as_nxt[mi] = __builtin_amdgcn_raw_buffer_load_b128(asr, aoff[mi] + 16 * c, 0, 0);
+  };
+  auto next_quad_scales = [&]() {
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
       uint32_t v = 0;
@@ -149,14 +189,8 @@ __device__ __forceinline__ void mx_tiled_tile(const GroupedGemm& g, uint8_t* sme
       for (int u = 0; u < 4; ++u) v |= ((as_nxt[mi][u] >> (8 * kb)) & 0xffu) << (8 * u);
       as_cur[mi] = v;
     }
-  };
-  auto load_scales = [&](u32x4* as, uint32_t* ws, int c) {  // quad c
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni)
-      ws[ni] = __builtin_amdgcn_raw_buffer_load_b32(wsr, lane * 4, (wq[ni] * nq + c) * 256, 0);
-#pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-      as[mi] = __builtin_amdgcn_raw_buffer_load_b128(asr, aoff[mi] + 16 * c, 0, 0);
+    for (int ni = 0; ni < NT; ++ni) ws_cur[ni] = ws_nxt[ni];
   };
 
   // ---- fragments (LDS -> registers) --------------------------------------
@@ -186,41 +220,43 @@ __device__ __forceinline__ void mx_tiled_tile(const GroupedGemm& g, uint8_t* sme
   };
 
   f32x4 acc[MT][NT];
-#pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  MxTileInfo cur = locate(t), nxt = cur;
+  uint32_t cur_adma[C::LPA], cur_aoff[MT], nxt_adma[C::LPA], nxt_aoff[MT];
   int c_cur = 0, kt_base = 0;  // current quad and its first step
 
   // ---- pipeline ------------------------------------------------------------
-  // Quad 0's scales first, then stages 0 .. 3 (ns >= 4).  Step kt (stage
-  // buffer kt % 4): the fragments of step kt are in registers (read one step
-  // earlier); wait until this wave's DMA of stage kt+1 is done; barrier (stage
-  // kt+1 complete for every wave, stage kt's buffer read by every wave); DMA
-  // of step kt+4 into stage kt's buffer; read step kt+1's fragments; MFMAs of
-  // step kt.  The explicit vmcnt waits count only the DMA loads (the scale
-  // loads in between only make them stricter).  The last quad is peeled off,
-  // so every wait count is a constant and the loop body has no branch (a
-  // branch would let the MFMAs be moved past the barriers).
-  auto step = [&](auto U, auto LAST) {
+  // Step kt (stage buffer kt % 4): the fragments of step kt are in registers
+  // (read one step earlier); wait until this wave's DMA of stage kt+1 is
+  // done; barrier (stage kt+1 complete for every wave, stage kt's buffer read
+  // by every wave); DMA into stage kt's buffer (this tile's step kt+4, or in
+  // the last quad the next tile's step kt % 4); read step kt+1's fragments;
+  // MFMAs of step kt.  Every wait counts only DMA loads (8 per wave and step,
+  // issued after the target on every path: two later steps' worth); other
+  // loads and stores in between only make it stricter.  The block's last tile
+  // streams its own first steps in again as "next" (in-bounds reads that are
+  // never used; drained before the block exits), so that the last quad has one
+  // form.  Each step is straight-line code: a branch inside would let the
+  // MFMAs be moved past the barriers.
+  enum { MID = 0, LAST = 1 };
+  auto step = [&](auto U, auto MODE) {
     constexpr int u = decltype(U)::value;
-    constexpr bool last = decltype(LAST)::value;
+    constexpr int mode = decltype(MODE)::value;
     constexpr int f = u & 1;
     // this wave's fragment reads of stage kt must land before the barrier
     use_frags<MT>(af[f]);
     use_regs<NT>(wf[f]);
-    if (!last || u == 0)
-      wait_vm<2 * C::LPW>();  // stages kt+2, kt+3 may stay in flight
-    else if (u == 1)
-      wait_vm<C::LPW>();
-    else
-      wait_vm<0>();
+    // stages kt+2, kt+3 (or the next tile's first) may stay in flight; the
+    // last step of a tile has no stage to wait for
+    if (mode == MID || u < 3) wait_vm<2 * C::LPW>();
     block_barrier();
-    if (!last) {
-      issue(u, kt_base + u + 4);
-      if (u == 0) load_scales(as_nxt, ws_nxt, c_cur + 1);
+    if (mode == MID) {
+      issue(cur, cur_adma, u, kt_base + u + 4);
+      if (u == 0) load_scales(cur, cur_aoff, c_cur + 1);
+    } else {
+      issue(nxt, nxt_adma, u, u);
+      if (u == 0) load_scales(nxt, nxt_aoff, 0);
     }
-    if (!last || u < 3) read_frags(f ^ 1, (u + 1) & 3);
+    if (mode == MID || u < 3) read_frags(f ^ 1, (u + 1) & 3);
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
       const uint32_t xsc = (as_cur[mi] >> (8 * u)) & 0xffu;
@@ -233,14 +269,14 @@ __device__ __forceinline__ void mx_tiled_tile(const GroupedGemm& g, uint8_t* sme
     // the scale loads at the start of a quad), then one MFMA and two LDS
     // reads, and so on: with one wave per SIMD the memory instructions issue
     // while the matrix core works instead of before it.
-    if (!last) {
+    {
 #pragma unroll
       for (int i = 0; i < C::LPW + (u == 0 ? MT + NT : 0); ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
       }
     }
-    if (!last || u < 3) {
+    if (mode == MID || u < 3) {
 #pragma unroll
       for (int i = 0; i < (2 * MT + NT) / 2; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -253,115 +289,118 @@ __device__ __forceinline__ void mx_tiled_tile(const GroupedGemm& g, uint8_t* sme
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  using Mid = std::integral_constant<bool, false>;
-  using Last = std::integral_constant<bool, true>;
+  using Mid = std::integral_constant<int, MID>;
+  using Last = std::integral_constant<int, LAST>;
 
-  load_scales(as_nxt, ws_cur, 0);
-  compact();
+  // first tile: its gathers, stages 0..3 and first scale quad
+  gather(cur, cur_adma, cur_aoff);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) issue(p, p);
-  wait_vm<3 * C::LPW>();
-  block_barrier();
-  read_frags(0, 0);
-  for (c_cur = 0; c_cur < nq - 1; ++c_cur) {
+  for (int p = 0; p < 4; ++p) issue(cur, cur_adma, p, p);
+  load_scales(cur, cur_aoff, 0);
+
+  for (;;) {
+    const int tn = t + (int)gridDim.x;
+    const bool has_next = tn < total;
+    if (has_next) nxt = locate(tn);
+    gather(nxt, nxt_adma, nxt_aoff);  // (the current tile again when there is no next)
+    next_quad_scales();
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // stage 0 of this tile: stages 1..3 were issued after it
+    wait_vm<3 * C::LPW>();
+    block_barrier();
+    read_frags(0, 0);
+    c_cur = 0;
+    do {  // quads 0 .. nq-2 (nq >= 2)
+      kt_base = 4 * c_cur;
+      step(I0{}, Mid{});
+      step(I1{}, Mid{});
+      step(I2{}, Mid{});
+      step(I3{}, Mid{});
+      next_quad_scales();
+    } while (++c_cur < nq - 1);
     kt_base = 4 * c_cur;
-    step(I0{}, Mid{});
-    step(I1{}, Mid{});
-    step(I2{}, Mid{});
-    step(I3{}, Mid{});
-    compact();
+    step(I0{}, Last{});
+    step(I1{}, Last{});
+    step(I2{}, Last{});
+    step(I3{}, Last{});
+    // (The accumulators are pinned here so that the last MFMAs are not sunk
+    // into the row-guarded stores below.)
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) ws_cur[ni] = ws_nxt[ni];
-  }
-  kt_base = 4 * c_cur;
-  step(I0{}, Last{});
-  step(I1{}, Last{});
-  step(I2{}, Last{});
-  step(I3{}, Last{});
-  // Every DMA and LDS read of this tile has completed before the last
-  // barrier: the next tile may refill the ring.  (The accumulators are
-  // pinned here so that the last MFMAs are not sunk into the row-guarded
-  // stores below.)
+    for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NT; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
+      for (int ni = 0; ni < NT; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
 
-  // ---- epilogue (registers -> global) -------------------------------------
-  // D[n][m]: lane (li, kb) holds activation row li of group mi and, for
-  // weight group ni, weight rows (= output columns) 4 kb .. 4 kb + 3.
+    // ---- epilogue (registers -> global) -----------------------------------
+    // D[n][m]: lane (li, kb) holds activation row li of group mi and, for
+    // weight group ni, weight rows (= output columns) 4 kb .. 4 kb + 3.
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi) {
-    const int r = 16 * (mi * WM + wm) + li;
-    if (SWIGLU) {
+    for (int mi = 0; mi < MT; ++mi) {
+      const int r = 16 * (mi * WM + wm) + li;
+      if (SWIGLU) {
 #pragma unroll
-      for (int b = 0; b < NT / 4; ++b) {
-        const f32x4 g0 = acc[mi][2 * b], g1 = acc[mi][2 * b + 1];
-        const f32x4 u0 = acc[mi][NT / 2 + 2 * b], u1 = acc[mi][NT / 2 + 2 * b + 1];
-        float a[8];
+        for (int b = 0; b < NT / 4; ++b) {
+          const f32x4 g0 = acc[mi][2 * b], g1 = acc[mi][2 * b + 1];
+          const f32x4 u0 = acc[mi][NT / 2 + 2 * b], u1 = acc[mi][NT / 2 + 2 * b + 1];
+          float a[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a[i] = silu_fast(g0[i]) * u0[i];
-          a[4 + i] = silu_fast(g1[i]) * u1[i];
+          for (int i = 0; i < 4; ++i) {
+            a[i] = silu_fast(g0[i]) * u0[i];
+            a[4 + i] = silu_fast(g1[i]) * u1[i];
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+          amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+          const int e = mx_exponent(amax);
+          const float inv = exp2_neg(e);
+          const uint32_t lo = e4m3_pack4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+          const uint32_t hi = e4m3_pack4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv);
+          if (r < cur.nrows) {
+            const int col0 = cur.n0 + 16 * (wn * (NT / 2) + 2 * b);
+            uint8_t* orow = static_cast<uint8_t*>(g.out) + (size_t)(cur.row0 + r) * g.N;
+            *reinterpret_cast<uint32_t*>(orow + col0 + 4 * kb) = lo;
+            *reinterpret_cast<uint32_t*>(orow + col0 + 16 + 4 * kb) = hi;
+            if (kb == 0)
+              g.out_scales[(size_t)(cur.row0 + r) * (g.N / 32) + col0 / 32] = (uint8_t)(e + 127);
+          }
         }
-        float amax = 0.f;
+      } else if (r < cur.nrows) {
+        uint16_t* orow = static_cast<uint16_t*>(g.out) + (size_t)(cur.row0 + r) * g.N + cur.n0 +
+                         16 * wn * NT + 4 * kb;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        const int e = mx_exponent(amax);
-        const float inv = exp2_neg(e);
-        const uint32_t lo = e4m3_pack4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
-        const uint32_t hi = e4m3_pack4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv);
-        if (r < nrows) {
-          const int col0 = n0 + 16 * (wn * (NT / 2) + 2 * b);
-          uint8_t* orow = static_cast<uint8_t*>(g.out) + (size_t)(row0 + r) * g.N;
-          *reinterpret_cast<uint32_t*>(orow + col0 + 4 * kb) = lo;
-          *reinterpret_cast<uint32_t*>(orow + col0 + 16 + 4 * kb) = hi;
-          if (kb == 0) g.out_scales[(size_t)(row0 + r) * (g.N / 32) + col0 / 32] = (uint8_t)(e + 127);
+        for (int ni = 0; ni < NT; ++ni) {
+          u32x2 pk;
+          pk.x = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
+          pk.y = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
+          *reinterpret_cast<u32x2*>(orow + 16 * ni) = pk;
         }
-      }
-    } else if (r < nrows) {
-      uint16_t* orow = static_cast<uint16_t*>(g.out) + (size_t)(row0 + r) * g.N + n0 +
-                       16 * wn * NT + 4 * kb;
-#pragma unroll
-      for (int ni = 0; ni < NT; ++ni) {
-        u32x2 pk;
-        pk.x = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
-        pk.y = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
-        *reinterpret_cast<u32x2*>(orow + 16 * ni) = pk;
       }
     }
-  }
-}
-
-template <bool SWIGLU, int WM, int WN, int NS>
-__global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, int n_tiles) {
-  using C = MxTiled<SWIGLU, WM, WN, NS>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE];
-  TileMap tm;
-  tm.init(g.offsets, g.G, g.ident_rows, C::BM, g.total_rows);
-  const int total = tm.total * n_tiles;
-  // Expert-major tile order (as in the bf16 tiled kernel): the m-tiles that
-  // share a weight tile are neighbours, and an expert's tiles stay on one XCD.
-  for (int t = blockIdx.x; t < total; t += gridDim.x) {
-    const int id = xcd_remap(t, total);
-    int grp, first_mt, n_mt, grow0, grow1;
-    tm.find_group(id / n_tiles, grp, first_mt, n_mt, grow0, grow1);
-    const int local = id - first_mt * n_tiles;
-    const int n_tile = local / n_mt;
-    const int row0 = grow0 + (local - n_tile * n_mt) * C::BM;
-    mx_tiled_tile<SWIGLU, WM, WN, NS>(g, smem, __builtin_amdgcn_readfirstlane(n_tile),
-                                      __builtin_amdgcn_readfirstlane(grp),
-                                      __builtin_amdgcn_readfirstlane(row0),
-                                      __builtin_amdgcn_readfirstlane(min(C::BM, grow1 - row0)));
+    if (!has_next) {
+      wait_vm<0>();  // the repeated first steps: no DMA may outlive the block's LDS
+      break;
+    }
+    t = tn;
+    cur = nxt;
+#pragma unroll
+    for (int i = 0; i < C::LPA; ++i) cur_adma[i] = nxt_adma[i];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) cur_aoff[mi] = nxt_aoff[mi];
   }
 }
 
 // Shapes the tiled kernels take: whole 128-column (GEMM1) / 256-column
-// (GEMM2) output tiles and K a multiple of 512 (whole quads of steps).
+// (GEMM2) output tiles, K a multiple of 512 (whole quads of steps) with at
+// least two quads (the last quad of a tile is peeled off the loop), and
+// activation offsets that fit 32 bits.
 bool mx_tiled_fits(const GroupedGemm& g, bool swiglu) {
-  return g.N % (swiglu ? 128 : 256) == 0 && g.K % 512 == 0;
+  const long long arows = g.gather ? g.total_rows / g.topk : g.total_rows;
+  return g.N % (swiglu ? 128 : 256) == 0 && g.K % 512 == 0 && g.K >= 1024 &&
+         arows * g.K < (1ll << 32);
 }
 
 template <bool SWIGLU, int WM, int WN, int NS>

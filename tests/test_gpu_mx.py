@@ -27,16 +27,21 @@ SMALL = {
     # Hy3-style gate with an always-on W4A8 shared expert
     "mx_shared": CFG["hy3"].with_(name="mx_shared", T=40, H=512, E=16, k=4, I=256, shared_I=384,
                                   fmt="w4a8", family_seed=1108, x_seed=25),
-    # more than 16 rows per expert and K a multiple of 512: the LDS-tiled
-    # kernels; one quad of K-steps per tile (the peeled last quad only) ...
-    "mx_tiled": CFG["qwen3_decode_w4a8"].with_(name="mx_tiled", T=512, H=512, E=8, k=2, I=512,
+    # more than 16 rows per expert and K a multiple of 512, at least 1024:
+    # the LDS-tiled kernels; two quads of K-steps per tile ...
+    "mx_tiled": CFG["qwen3_decode_w4a8"].with_(name="mx_tiled", T=512, H=1024, E=8, k=2, I=1024,
                                                family_seed=1109, x_seed=26),
     # ... several quads, ragged 128-row m-tiles, 8 n-tiles in each GEMM
     "mx_tiled_deep": CFG["qwen3_decode_w4a8"].with_(name="mx_tiled_deep", T=300, H=2048, E=4, k=2,
                                                     I=1024, family_seed=1110, x_seed=27),
-    # shared expert (one identity group of T rows) on the tiled kernels too
+    # shared expert (one identity group of T rows) on the tiled GEMM1; GEMM2
+    # has K = 512 (streaming kernels)
     "mx_tiled_shared": CFG["hy3"].with_(name="mx_tiled_shared", T=200, H=1024, E=8, k=4, I=512,
                                         shared_I=512, fmt="w4a8", family_seed=1111, x_seed=28),
+    # more tiles than resident blocks: blocks stream from one tile into the
+    # next (the next tile's first steps load during the current one's last)
+    "mx_tiled_stream": CFG["qwen3_decode_w4a8"].with_(name="mx_tiled_stream", T=1024, H=2048, E=4,
+                                                      k=4, I=2048, family_seed=1112, x_seed=29),
 }
 
 
@@ -188,7 +193,7 @@ def test_mx_layer_full_prefill():
     _layer_check(CFG["qwen3_prefill_w4a8"], tokens=[0, 1, 2, 777, 2048, 4094, 4095])
 
 
-@pytest.mark.parametrize("name", ["mx_tiled", "mx_tiled_deep"])
+@pytest.mark.parametrize("name", ["mx_tiled", "mx_tiled_deep", "mx_tiled_stream"])
 def test_mx_tiled_equals_streaming_bit_for_bit(name):
     """A row's GEMM outputs depend only on that row, and both GEMM kernels
     run the same scaled MFMAs over the same K-steps in the same order.  With
