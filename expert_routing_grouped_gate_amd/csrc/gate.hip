@@ -136,8 +136,7 @@ __global__ __launch_bounds__(64) void router_partial(const uint16_t* __restrict_
       float amax = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      amax = max_lanes_16_32(amax);
       const int ex = mx_exponent(amax);
       const float inv = exp2_neg(ex);
       const uint32_t lo = e4m3_pack4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);

@@ -254,8 +254,7 @@ __device__ __forceinline__ void mx_store(const GroupedGemm& g, const MxTile& t, 
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    amax = max_lanes_16_32(amax);
     const int e = mx_exponent(amax);
     const float inv = exp2_neg(e);
     const uint32_t lo = e4m3_pack4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);

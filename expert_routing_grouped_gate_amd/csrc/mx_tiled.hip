@@ -89,7 +89,12 @@ template <bool SWIGLU, int WM, int WN, int NS>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, int n_tiles) {
   using C = MxTiled<SWIGLU, WM, WN, NS>;
   constexpr int MT = C::MT, NT = C::NT;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE];
+  // One LDS array: the ring, then the scheduler's per-lane table (13 values
+  // per lane, one copy per wave), parked here between tiles, where it costs
+  // no registers in the K loop.  (A second __shared__ variable makes the
+  // compiler wait for every outstanding DMA to LDS before each LDS read.)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE + C::NW * 13 * 64 * 4];
+  int(*tm_lds)[13][64] = reinterpret_cast<int(*)[13][64]>(smem + NS * C::STAGE);
   TileMap tm;
   tm.init(g.offsets, g.G, g.ident_rows, C::BM, g.total_rows);
   const int total = __builtin_amdgcn_readfirstlane(tm.total * n_tiles);
@@ -99,9 +104,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (g.offsets != nullptr) {
+    int* mine = &tm_lds[wave][0][lane];
+    mine[0] = tm.excl;
+    mine[64] = tm.gbeg;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) mine[64 * (2 + i)] = tm.tiles[i];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) mine[64 * (7 + i)] = tm.o[i];
+  }
   const int wm = wave % WM, wn = wave / WM;
   const int li = lane & 15, kb = lane >> 4;
-  const int K = g.K, ns = K / 128, nq = ns / 4;  // nq >= 2
+  const int K = g.K, ns = K / 128, nq = ns / 4;  // nq >= 2 (launcher)
   const uint8_t* A = static_cast<const uint8_t*>(g.A);
   const int arows_total = g.gather ? g.total_rows / g.topk : g.total_rows;
   const __amdgpu_buffer_rsrc_t asr = mx_rsrc(g.A_scales, (uint32_t)arows_total * (uint32_t)(K / 32));
@@ -110,8 +124,22 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
 
   auto locate = [&](int tt) {
     const int id = xcd_remap(tt, total);
+    TileMap tl;
+    tl.offsets = g.offsets;
+    tl.ident_rows = g.ident_rows;
+    tl.total = tm.total;
+    tl.BM = C::BM;
+    if (g.offsets != nullptr) {
+      const int* mine = &tm_lds[wave][0][lane];
+      tl.excl = mine[0];
+      tl.gbeg = mine[64];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) tl.tiles[i] = mine[64 * (2 + i)];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) tl.o[i] = mine[64 * (7 + i)];
+    }
     int grp, first_mt, n_mt, grow0, grow1;
-    tm.find_group(id / n_tiles, grp, first_mt, n_mt, grow0, grow1);
+    tl.find_group(id / n_tiles, grp, first_mt, n_mt, grow0, grow1);
     const int local = id - first_mt * n_tiles;
     const int n_tile = local / n_mt;
     const int row0 = grow0 + (local - n_tile * n_mt) * C::BM;
@@ -122,44 +150,65 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
     ti.nrows = __builtin_amdgcn_readfirstlane(min(C::BM, grow1 - row0));
     return ti;
   };
-  // Per-lane row offsets of a tile: adma[i] = byte offset in A of the 16
-  // bytes this lane's DMA i reads at step 0 (activation group ra = wave +
-  // NW i, 8 rows; lane l fills row 8 ra + l/8, physical chunk l % 8, i.e. it
-  // loads logical chunk (l % 8) ^ (l / 8)); aoff[mi] = byte offset of the
-  // scale row of this lane's activation row in fragment group mi.  Rows past
-  // the tile end reuse a valid row.
-  auto gather = [&](const MxTileInfo& ti, uint32_t* adma, uint32_t* aoff) {
+  // Per-lane rows of a tile, in two halves so that no load result is used
+  // right after its load.  gather_issue: the sorted row of each of this lane's
+  // LPA DMA rows (activation group ra = wave + NW i, 8 rows; lane l fills row
+  // 8 ra + l/8) and MT fragment rows, and with a gather the pair ids stored
+  // there, all loads issued together.  gather_finish: adma[i] = byte offset
+  // in A of the 16 bytes DMA i reads at step 0 (physical chunk l % 8 holds
+  // logical chunk (l % 8) ^ (l / 8)); aoff[mi] = byte offset of the scale row
+  // of fragment row mi.  Rows past the tile end reuse a valid row; pair ids
+  // are clamped into the token range.
+  constexpr int NRAW = C::LPA + MT;
+  auto gather_issue = [&](const MxTileInfo& ti, int* raw) {
+    int r[NRAW];
 #pragma unroll
-    for (int i = 0; i < C::LPA; ++i) {
-      const int row = 8 * (wave + C::NW * i) + (lane >> 3);
-      const int r = ti.row0 + min(row, ti.nrows - 1);
-      const uint32_t arow = (uint32_t)gather_row(g.sorted_pair, g.gather, g.topk, g.total_rows, r);
-      adma[i] = arow * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
-    }
+    for (int i = 0; i < C::LPA; ++i) r[i] = ti.row0 + min(8 * (wave + C::NW * i) + (lane >> 3), ti.nrows - 1);
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-      const int r = ti.row0 + min(16 * (mi * WM + wm) + li, ti.nrows - 1);
-      aoff[mi] = (uint32_t)gather_row(g.sorted_pair, g.gather, g.topk, g.total_rows, r) *
-                 (uint32_t)(K / 32);
+    for (int mi = 0; mi < MT; ++mi) r[C::LPA + mi] = ti.row0 + min(16 * (mi * WM + wm) + li, ti.nrows - 1);
+    if (g.gather) {
+#pragma unroll
+      for (int j = 0; j < NRAW; ++j) raw[j] = g.sorted_pair[r[j]];
+    } else {
+#pragma unroll
+      for (int j = 0; j < NRAW; ++j) raw[j] = r[j];
     }
   };
-  // DMA of step st of tile ti into stage buffer buf: LPA activation groups
-  // and LPB weight blocks of 1 KB per wave.
-  auto issue = [&](const MxTileInfo& ti, const uint32_t* adma, int buf, int st) {
-    uint8_t* stg = smem + buf * C::STAGE;
-    const uint8_t* Wg = static_cast<const uint8_t*>(g.W) + (size_t)ti.grp * g.w_gstride;
+  auto gather_finish = [&](const int* raw, uint32_t* adma, uint32_t* aoff) {
+    uint32_t arow[NRAW];
+#pragma unroll
+    for (int j = 0; j < NRAW; ++j)
+      arow[j] = g.gather ? (uint32_t)min(max(raw[j], 0) / g.topk, g.total_rows / g.topk - 1)
+                         : (uint32_t)raw[j];
 #pragma unroll
     for (int i = 0; i < C::LPA; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(A + (size_t)adma[i] + st * 128),
-          (__attribute__((address_space(3))) void*)(stg + (wave + C::NW * i) * 1024), 16, 0, 0);
+      adma[i] = arow[i] * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) aoff[mi] = arow[C::LPA + mi] * (uint32_t)(K / 32);
+  };
+  // DMA of step st of tile ti into stage buffer buf: LPA activation groups
+  // and LPB weight blocks of 1 KB per wave, as buffer loads to LDS: the
+  // per-lane part of each address is a VGPR that lives for the whole tile
+  // (adma[i], or lane*16 for the weights) and the per-step part a scalar
+  // offset, so no address register is rebuilt (and reused) every step.
+  const __amdgpu_buffer_rsrc_t ar = mx_rsrc(A, (uint32_t)arows_total * (uint32_t)K);
+  const uint32_t wbytes = wrows * (uint32_t)(K / 2);
+  const uint32_t wlane = (uint32_t)lane * 16u;
+  auto issue = [&](const MxTileInfo& ti, const uint32_t* adma, int buf, int st) {
+    uint8_t* stg = smem + buf * C::STAGE;
+    const __amdgpu_buffer_rsrc_t wr =
+        mx_rsrc(static_cast<const uint8_t*>(g.W) + (size_t)ti.grp * g.w_gstride, wbytes);
+#pragma unroll
+    for (int i = 0; i < C::LPA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ar, (__attribute__((address_space(3))) void*)(stg + (wave + C::NW * i) * 1024), 16,
+          adma[i], st * 128, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::LPB; ++i) {
       const int q = mx_block_row<SWIGLU, C::BN>(g, ti.n0, wave + C::NW * i) / 16;
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(Wg + (size_t)(q * ns + st) * 1024 + lane * 16),
-          (__attribute__((address_space(3))) void*)(stg + C::ABYTES + (wave + C::NW * i) * 1024),
-          16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (__attribute__((address_space(3))) void*)(stg + C::ABYTES + (wave + C::NW * i) * 1024),
+          16, wlane, (q * ns + st) * 1024, 0, 0);
     }
   };
 
@@ -219,9 +268,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
     for (int ni = 0; ni < NT; ++ni) wf[f][ni] = *reinterpret_cast<const u32x4*>(stg + wread[ni]);
   };
 
-  f32x4 acc[MT][NT];
   MxTileInfo cur = locate(t), nxt = cur;
   uint32_t cur_adma[C::LPA], cur_aoff[MT], nxt_adma[C::LPA], nxt_aoff[MT];
+  int nxt_raw[NRAW];
   int c_cur = 0, kt_base = 0;  // current quad and its first step
 
   // ---- pipeline ------------------------------------------------------------
@@ -238,7 +287,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
   // form.  Each step is straight-line code: a branch inside would let the
   // MFMAs be moved past the barriers.
   enum { MID = 0, LAST = 1 };
-  auto step = [&](auto U, auto MODE) {
+  auto step = [&](f32x4 (&acc)[MT][NT], auto U, auto MODE) {
     constexpr int u = decltype(U)::value;
     constexpr int mode = decltype(MODE)::value;
     constexpr int f = u & 1;
@@ -248,6 +297,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
     // stages kt+2, kt+3 (or the next tile's first) may stay in flight; the
     // last step of a tile has no stage to wait for
     if (mode == MID || u < 3) wait_vm<2 * C::LPW>();
+    if (mode == MID && u == 3) {
+      // This wait has also retired the scale loads of step 0 (issued before
+      // the DMA of step 1 of this quad) and the next tile's row loads (issued
+      // when this tile started): mark them as read here, so that the
+      // compiler's own waits for them (where paths merge) do not drain the ring.
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) asm volatile("" : "+v"(ws_nxt[ni]));
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) asm volatile("" : "+v"(as_nxt[mi]));
+#pragma unroll
+      for (int j = 0; j < NRAW; ++j) asm volatile("" : "+v"(nxt_raw[j]));
+    }
     block_barrier();
     if (mode == MID) {
       issue(cur, cur_adma, u, kt_base + u + 4);
@@ -292,40 +353,49 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
   using Mid = std::integral_constant<int, MID>;
   using Last = std::integral_constant<int, LAST>;
 
-  // first tile: its gathers, stages 0..3 and first scale quad
-  gather(cur, cur_adma, cur_aoff);
-#pragma unroll
-  for (int p = 0; p < 4; ++p) issue(cur, cur_adma, p, p);
+  // first tile: its rows, then stage 0, its first scale quad and stages 1..3
+  // (the order in which the last quad of a tile starts the next one)
+  gather_issue(cur, nxt_raw);
+  gather_finish(nxt_raw, cur_adma, cur_aoff);
+  issue(cur, cur_adma, 0, 0);
   load_scales(cur, cur_aoff, 0);
+#pragma unroll
+  for (int p = 1; p < 4; ++p) issue(cur, cur_adma, p, p);
 
   for (;;) {
     const int tn = t + (int)gridDim.x;
     const bool has_next = tn < total;
     if (has_next) nxt = locate(tn);
-    gather(nxt, nxt_adma, nxt_aoff);  // (the current tile again when there is no next)
-    next_quad_scales();
+    gather_issue(nxt, nxt_raw);  // (the current tile again when there is no next)
+    f32x4 acc[MT][NT];  // (scoped to the tile: no accumulator value crosses tiles)
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // stage 0 of this tile: stages 1..3 were issued after it
+    // stage 0 of this tile: stages 1..3 were issued after it, and after this
+    // tile's first scale quad, which this wait therefore retires as well
     wait_vm<3 * C::LPW>();
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) asm volatile("" : "+v"(ws_nxt[ni]));
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) asm volatile("" : "+v"(as_nxt[mi]));
+    next_quad_scales();
     block_barrier();
     read_frags(0, 0);
-    c_cur = 0;
-    do {  // quads 0 .. nq-2 (nq >= 2)
+    for (c_cur = 0; c_cur < nq - 1; ++c_cur) {  // quads 0 .. nq-2
       kt_base = 4 * c_cur;
-      step(I0{}, Mid{});
-      step(I1{}, Mid{});
-      step(I2{}, Mid{});
-      step(I3{}, Mid{});
+      step(acc, I0{}, Mid{});
+      step(acc, I1{}, Mid{});
+      step(acc, I2{}, Mid{});
+      step(acc, I3{}, Mid{});
       next_quad_scales();
-    } while (++c_cur < nq - 1);
+    }
     kt_base = 4 * c_cur;
-    step(I0{}, Last{});
-    step(I1{}, Last{});
-    step(I2{}, Last{});
-    step(I3{}, Last{});
+    gather_finish(nxt_raw, nxt_adma, nxt_aoff);
+    step(acc, I0{}, Last{});
+    step(acc, I1{}, Last{});
+    step(acc, I2{}, Last{});
+    step(acc, I3{}, Last{});
     // (The accumulators are pinned here so that the last MFMAs are not sunk
     // into the row-guarded stores below.)
 #pragma unroll
@@ -353,8 +423,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
           float amax = 0.f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
-          amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-          amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+          amax = max_lanes_16_32(amax);
           const int e = mx_exponent(amax);
           const float inv = exp2_neg(e);
           const uint32_t lo = e4m3_pack4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);

@@ -20,13 +20,28 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // the sign of zero; clamping to +-448 first gives the saturation.  This equals
 // an integer implementation of the rule on every fp32 input (an exhaustive
 // check over all 2^32 bit patterns on gfx950).  Byte i = code of value i.
+// The clamp works on the bits: the magnitude (an integer that orders like
+// the float) is limited to 448's, which maps inf and NaN to 448 as well, and
+// the sign is put back; no branch.
 __device__ __forceinline__ float e4m3_clamp(float v) {
-  return __builtin_isnan(v) ? __builtin_copysignf(448.f, v) : fminf(fmaxf(v, -448.f), 448.f);
+  const uint32_t bits = __float_as_uint(v);
+  const uint32_t mag = min(bits & 0x7fffffffu, 0x43e00000u);  // 0x43e00000 = 448.0f
+  return __uint_as_float(mag | (bits & 0x80000000u));
 }
 
 __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
   const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), lo, true);
+}
+
+// Maximum of x over lanes l, l^16, l^32, l^48 (the four lanes that hold one
+// row's 32-column block in the MFMA output layout), with the gfx950 row and
+// half-wave swaps (VALU) instead of LDS-routed shuffles.  Every lane active.
+__device__ __forceinline__ float max_lanes_16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // SiLU(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (about one
