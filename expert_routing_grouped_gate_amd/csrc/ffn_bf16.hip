@@ -391,6 +391,8 @@ static void launch_tiled(const GroupedGemm& g, hipStream_t s) {
 int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (small_m)
     launch_skinny<true, 1, 4, 4>(g, s);
+  else if (tiled4_fits(g, true))
+    launch_tiled4(g, true, s);
   else
     launch_tiled<true, 128, 256, 2, 4, 3, 1>(g, s);
   return launch_status();
@@ -399,6 +401,8 @@ int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
 int launch_ffn_down_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (small_m)
     launch_skinny<false, 4, 1, 4>(g, s);
+  else if (tiled4_fits(g, false))
+    launch_tiled4(g, false, s);
   else
     launch_tiled<false, 128, 256, 2, 4, 3, 1>(g, s);
   return launch_status();

@@ -69,6 +69,10 @@ int launch_ffn_down_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s);
 // LDS-tiled W4A8 GEMMs (128 x 256 block tiles) and the shapes they take.
 bool mx_tiled_fits(const GroupedGemm& g, bool swiglu);
 void launch_mx_tiled(const GroupedGemm& g, bool swiglu, hipStream_t s);
+// bf16 GEMMs for many rows per expert on one wave per SIMD (128 x 256 block
+// tiles, a DMA ring streaming across tiles) and the shapes they take.
+bool tiled4_fits(const GroupedGemm& g, bool swiglu);
+void launch_tiled4(const GroupedGemm& g, bool swiglu, hipStream_t s);
 
 int launch_mx_quantize(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
                        hipStream_t s);

@@ -1,0 +1,366 @@
+// S5/S6 for experts with many rows (prefill): bf16 grouped GEMMs on
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation, one wave per SIMD.
+//
+// [Qwen3] "GMM enablement and routing optimisation": one grouped matmul over
+// all experts; "MoE TP optimisation -> compute decomposition": w13 = gate
+// rows then up rows, SwiGLU = SiLU(first half) * second half, fused into the
+// GEMM1 epilogue.  Same arithmetic as the 8-wave tiled kernels of
+// ffn_bf16.hip (identical accumulation order, so identical results); only the
+// data movement and the schedule differ.
+//
+// Block tile: BM = 128 activation rows x BN = 256 weight rows (GEMM1: the 128
+// gate rows n0.. and the matching 128 up rows, 128 output columns; GEMM2: 256
+// output columns), K step 64.  Four waves (2 x 2), each a 64 x 128 sub-tile
+// of 4 x 8 MFMAs whose accumulators (128 per lane) live in AGPRs.  One LDS
+// stage (48 KB) holds the step's 128 activation rows then 256 weight rows,
+// 128 B each, the 16-byte chunk c of row r at chunk c ^ (r & 7).  Stages are
+// filled by buffer loads to LDS (DMA): each wave instruction writes 1 KB = 8
+// rows; lane l takes row l / 8, physical chunk l % 8, so it loads logical
+// chunk (l % 8) ^ (l / 8).  The per-lane part of every DMA address is a
+// register fixed for the tile (gathered activation rows) or for the whole
+// kernel (weight rows); the step and the n-tile go in the scalar offset.
+//
+// The three LDS stages form one ring over the block's whole sequence of
+// K-steps: global step s sits in stage s % 3, and the last three steps of a
+// tile DMA the next tile's first three, so the stream never drains between
+// tiles.  Fragments are read from LDS a half-step (K = 32) ahead of the
+// MFMAs that use them.
+#include "common.hpp"
+#include "launch.hpp"
+#include "mxfmt.hpp"
+
+namespace moe {
+
+template <bool SWIGLU>
+struct Tiled4 {
+  static constexpr int BM = 128, BN = 256, WM = 2, WN = 2, NW = 4, NTHR = 256;
+  static constexpr int MT = BM / 16 / WM;  // activation groups per wave (4)
+  static constexpr int NT = BN / 16 / WN;  // weight groups per wave (8)
+  static constexpr int BNOUT = SWIGLU ? BN / 2 : BN;
+  static constexpr int ABYTES = BM * 128;
+  static constexpr int STAGE = (BM + BN) * 128;  // bytes
+  static constexpr int NS = 3;
+  static constexpr int LPA = BM / 8 / NW;  // 1 KB activation DMAs per wave per stage (4)
+  static constexpr int LPB = BN / 8 / NW;  // 1 KB weight DMAs per wave per stage (8)
+  static constexpr int LPW = LPA + LPB;
+  static constexpr int TMW = 13;           // parked scheduler words per lane
+  static_assert(NS * STAGE + NW * TMW * 64 * 4 <= 160 * 1024, "LDS");
+};
+
+struct T4Tile {
+  int grp, n0, row0, nrows;  // wave-uniform
+};
+
+// Half-step fragments: MT activation and NT weight operands of 16 B.
+template <int MT, int NT>
+struct Frags {
+  u32x4 a[MT];
+  u32x4 b[NT];
+};
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles) {
+  using C = Tiled4<SWIGLU>;
+  constexpr int MT = C::MT, NT = C::NT, NW = C::NW;
+  // One LDS array: the ring, then the scheduler's per-lane table (one copy
+  // per wave), parked here between tiles where it costs no registers in the
+  // K loop.  (A second __shared__ variable makes the compiler wait for every
+  // outstanding DMA before each LDS read.)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE + NW * C::TMW * 64 * 4];
+  int(*tm_lds)[C::TMW][64] = reinterpret_cast<int(*)[C::TMW][64]>(smem + C::NS * C::STAGE);
+  TileMap tm;
+  tm.init(g.offsets, g.G, g.ident_rows, C::BM, g.total_rows);
+  const int total = __builtin_amdgcn_readfirstlane(tm.total * n_tiles);
+  int t = blockIdx.x;
+  if (t >= total) return;  // uniform per block: no barrier is left waiting
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (g.offsets != nullptr) {
+    int* mine = &tm_lds[wave][0][lane];
+    mine[0] = tm.excl;
+    mine[64] = tm.gbeg;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) mine[64 * (2 + i)] = tm.tiles[i];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) mine[64 * (7 + i)] = tm.o[i];
+  }
+  const int wm = wave % C::WM, wn = wave / C::WM;
+  const int li = lane & 15, kc = lane >> 4;
+  const int K = g.K, nk = K / 64;  // nk >= 5 (launcher)
+  const uint32_t rowb = 2u * (uint32_t)K;  // bytes per row
+  const int arows_total = g.gather ? g.total_rows / g.topk : g.total_rows;
+  const __amdgpu_buffer_rsrc_t ar = mx_rsrc(g.A, (uint32_t)arows_total * rowb);
+  const uint32_t wrows = SWIGLU ? 2u * (uint32_t)g.up_off : (uint32_t)g.N;
+  const uint32_t wbytes = wrows * rowb;
+  const uint32_t dchunk = 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+
+  auto locate = [&](int tt) {
+    const int id = xcd_remap(tt, total);
+    TileMap tl;
+    tl.offsets = g.offsets;
+    tl.ident_rows = g.ident_rows;
+    tl.total = tm.total;
+    tl.BM = C::BM;
+    if (g.offsets != nullptr) {
+      const int* mine = &tm_lds[wave][0][lane];
+      tl.excl = mine[0];
+      tl.gbeg = mine[64];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) tl.tiles[i] = mine[64 * (2 + i)];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) tl.o[i] = mine[64 * (7 + i)];
+    }
+    // expert-major, then n-tile, then the expert's m-tiles: the m-tiles that
+    // share a weight tile are neighbours, and an expert's tiles stay on one
+    // XCD (xcd_remap)
+    int grp, first_mt, n_mt, grow0, grow1;
+    tl.find_group(id / n_tiles, grp, first_mt, n_mt, grow0, grow1);
+    const int local = id - first_mt * n_tiles;
+    const int n_tile = local / n_mt;
+    const int row0 = grow0 + (local - n_tile * n_mt) * C::BM;
+    T4Tile ti;
+    ti.grp = __builtin_amdgcn_readfirstlane(grp);
+    ti.n0 = __builtin_amdgcn_readfirstlane(n_tile * C::BNOUT);
+    ti.row0 = __builtin_amdgcn_readfirstlane(row0);
+    ti.nrows = __builtin_amdgcn_readfirstlane(min(C::BM, grow1 - row0));
+    return ti;
+  };
+  // Activation rows of this lane's LPA DMAs (group ra = wave + NW i, 8 rows;
+  // lane l fills row 8 ra + l / 8), in two halves so that no loaded value is
+  // used right after its load: gather_issue loads the pair ids (rows past the
+  // tile end reuse a valid row), gather_finish turns them into byte offsets
+  // of the rows' step-0 chunk (pair ids clamped into the token range).
+  auto gather_issue = [&](const T4Tile& ti, int* raw) {
+    int r[C::LPA];
+#pragma unroll
+    for (int i = 0; i < C::LPA; ++i) r[i] = ti.row0 + min(8 * (wave + NW * i) + (lane >> 3), ti.nrows - 1);
+    if (g.gather) {
+#pragma unroll
+      for (int i = 0; i < C::LPA; ++i) raw[i] = g.sorted_pair[r[i]];
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::LPA; ++i) raw[i] = r[i];
+    }
+  };
+  auto gather_finish = [&](const int* raw, uint32_t* adma) {
+#pragma unroll
+    for (int i = 0; i < C::LPA; ++i) {
+      const uint32_t arow = g.gather ? (uint32_t)min(max(raw[i], 0) / g.topk, arows_total - 1)
+                                     : (uint32_t)raw[i];
+      adma[i] = arow * rowb + dchunk;
+    }
+  };
+  // Weight rows of this lane's LPB DMAs relative to the tile's n0 (group rb =
+  // wave + NW i of the 256 tile rows; GEMM1: rows 0..127 gate, 128..255 up).
+  uint32_t wdma[C::LPB];
+#pragma unroll
+  for (int i = 0; i < C::LPB; ++i) {
+    const int br = 8 * (wave + NW * i) + (lane >> 3);
+    const uint32_t row = SWIGLU ? (br < C::BN / 2 ? (uint32_t)br : (uint32_t)(g.up_off + br - C::BN / 2))
+                                : (uint32_t)br;
+    wdma[i] = row * rowb + dchunk;
+  }
+  const uint16_t* Wbase = static_cast<const uint16_t*>(g.W);
+  // DMA of step st of tile ti into stage buf.  (The builtin's offsets are
+  // int: an unsigned argument made the host pass drop the kernel's stub.)
+  auto issue = [&](const T4Tile& ti, const uint32_t* adma, int buf, int st) {
+    uint8_t* stg = smem + buf * C::STAGE;
+    const __amdgpu_buffer_rsrc_t wr = mx_rsrc(Wbase + (size_t)ti.grp * g.w_gstride, wbytes);
+    const uint32_t aso = (uint32_t)st * 128u;
+    const uint32_t wso = (uint32_t)ti.n0 * rowb + aso;
+#pragma unroll
+    for (int i = 0; i < C::LPA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ar, (__attribute__((address_space(3))) void*)(stg + (wave + NW * i) * 1024), 16, (int)adma[i],
+          (int)aso, 0, 0);
+#pragma unroll
+    for (int i = 0; i < C::LPB; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (__attribute__((address_space(3))) void*)(stg + C::ABYTES + (wave + NW * i) * 1024), 16,
+          (int)wdma[i], (int)wso, 0, 0);
+  };
+
+  // Fragment offsets in a stage for half-step h: activation row
+  // 64 wm + 16 mi + li, weight tile row (GEMM1) 64 wn + 16 ni + li for the
+  // gate groups ni < 4 and 128 + 64 wn + 16 (ni - 4) + li for the up groups,
+  // (GEMM2) 128 wn + 16 ni + li; 16-byte chunk 4 h + kc of the row.  Rows are
+  // multiples of 8 apart, so every row of a lane has the same swizzle.
+  int aoff[2], boff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ch = 16 * ((4 * h + kc) ^ (li & 7));
+    aoff[h] = (64 * wm + li) * 128 + ch;
+    boff[h] = C::ABYTES + ((SWIGLU ? 64 : 128) * wn + li) * 128 + ch;
+  }
+  auto bgroup = [](int ni) {
+    if (SWIGLU) return ni < NT / 2 ? ni * 2048 : (C::BN / 2) * 128 + (ni - NT / 2) * 2048;
+    return ni * 2048;
+  };
+  auto read_half = [&](Frags<MT, NT>& f, int buf, int h) {
+    const uint8_t* stg = smem + buf * C::STAGE;
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) f.a[mi] = *reinterpret_cast<const u32x4*>(stg + aoff[h] + mi * 2048);
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) f.b[ni] = *reinterpret_cast<const u32x4*>(stg + boff[h] + bgroup(ni));
+  };
+
+  T4Tile cur = locate(t), nxt = cur;
+  uint32_t cur_adma[C::LPA], nxt_adma[C::LPA];
+  int nxt_raw[C::LPA];
+  Frags<MT, NT> f0, f1;
+  int buf = 0;  // stage of the current step (global step % 3)
+
+  // One K-step.  On entry f0 holds the first half-step of the step's stage
+  // `buf`.  Read the second half into f1 while f0's MFMAs run; wait for this
+  // wave's DMA of the next stage (the one after it may stay in flight) and
+  // for f1; barrier (the next stage is complete for every wave, this stage
+  // has been read by every wave); DMA (ti, st) into this stage; read the next
+  // stage's first half into f0 while f1's MFMAs run.  Every wait counts only
+  // DMA loads (LPW per wave and step, one step's worth issued after the
+  // target on every path); other loads and stores in between only make it
+  // stricter.
+  auto step = [&](f32x4 (&acc)[MT][NT], const T4Tile& ti, const uint32_t* adma, int st) {
+    read_half(f1, buf, 1);
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = mfma16x16x32(f0.b[ni], f0.a[mi], acc[mi][ni]);
+#pragma unroll
+    for (int i = 0; i < MT + NT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    use_regs<MT>(f1.a);
+    use_regs<NT>(f1.b);
+    wait_vm<C::LPW>();
+    block_barrier();
+    issue(ti, adma, buf, st);
+    buf = buf == C::NS - 1 ? 0 : buf + 1;
+    read_half(f0, buf, 0);
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = mfma16x16x32(f1.b[ni], f1.a[mi], acc[mi][ni]);
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM (DMA)
+    }
+#pragma unroll
+    for (int i = 0; i < MT + NT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // first tile: its rows, then stages 0..2, then stage 0's first half
+  gather_issue(cur, nxt_raw);
+  gather_finish(nxt_raw, cur_adma);
+#pragma unroll
+  for (int p = 0; p < C::NS; ++p) issue(cur, cur_adma, p, p);
+  wait_vm<(C::NS - 1) * C::LPW>();
+  block_barrier();
+  read_half(f0, 0, 0);
+
+  for (;;) {
+    const int tn = t + (int)gridDim.x;
+    const bool has_next = tn < total;
+    if (has_next) nxt = locate(tn);
+    gather_issue(nxt, nxt_raw);  // (the current tile again when there is no next)
+    f32x4 acc[MT][NT];  // (scoped to the tile: no accumulator value crosses tiles)
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+    step(acc, cur, cur_adma, 3);
+    step(acc, cur, cur_adma, 4);
+    // The wait in step 1 retired every load issued before step 0's DMA,
+    // including the pair ids above: mark them read here, so that the
+    // compiler's own wait for them (where paths merge) does not drain the ring.
+#pragma unroll
+    for (int i = 0; i < C::LPA; ++i) asm volatile("" : "+v"(nxt_raw[i]));
+    gather_finish(nxt_raw, nxt_adma);
+    for (int kt = 2; kt < nk - 3; ++kt) step(acc, cur, cur_adma, kt + 3);
+    // the last three steps stream in the next tile's first three
+    step(acc, nxt, nxt_adma, 0);
+    step(acc, nxt, nxt_adma, 1);
+    step(acc, nxt, nxt_adma, 2);
+    // (pinned so that the last MFMAs are not sunk into the row-guarded stores)
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni) asm volatile("" : "+a"(acc[mi][ni]));
+
+    // ---- epilogue (registers -> global) -----------------------------------
+    // D[n][m]: lane (li, kc) holds activation row li of group mi and, for
+    // weight group ni, weight rows (= output columns) 4 kc .. 4 kc + 3.
+    uint16_t* out = static_cast<uint16_t*>(g.out);
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+      const int r = 64 * wm + 16 * mi + li;
+      if (r < cur.nrows) {
+        uint16_t* orow = out + (size_t)(cur.row0 + r) * g.N + cur.n0 + 4 * kc;
+        if (SWIGLU) {
+#pragma unroll
+          for (int ni = 0; ni < NT / 2; ++ni) {
+            const f32x4 gt = acc[mi][ni], up = acc[mi][ni + NT / 2];
+            u32x2 pk;
+            pk.x = pack_bf16x2(gt[0] / (1.f + expf(-gt[0])) * up[0], gt[1] / (1.f + expf(-gt[1])) * up[1]);
+            pk.y = pack_bf16x2(gt[2] / (1.f + expf(-gt[2])) * up[2], gt[3] / (1.f + expf(-gt[3])) * up[3]);
+            *reinterpret_cast<u32x2*>(orow + 64 * wn + 16 * ni) = pk;
+          }
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < NT; ++ni) {
+            u32x2 pk;
+            pk.x = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
+            pk.y = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
+            *reinterpret_cast<u32x2*>(orow + 128 * wn + 16 * ni) = pk;
+          }
+        }
+      }
+    }
+    if (!has_next) {
+      wait_vm<0>();  // the repeated first steps: no DMA may outlive the block's LDS
+      break;
+    }
+    t = tn;
+    cur = nxt;
+#pragma unroll
+    for (int i = 0; i < C::LPA; ++i) cur_adma[i] = nxt_adma[i];
+  }
+}
+
+// Shapes the kernel takes: whole output tiles, K a multiple of 64 with at
+// least 5 steps (two leading steps and the last three are peeled off the
+// loop), and operands addressable with 32-bit offsets.
+bool tiled4_fits(const GroupedGemm& g, bool swiglu) {
+  const long long arows = g.gather ? g.total_rows / g.topk : g.total_rows;
+  const long long wrows = swiglu ? 2ll * g.up_off : g.N;
+  return g.N % (swiglu ? 128 : 256) == 0 && g.K % 64 == 0 && g.K >= 320 &&
+         arows * g.K * 2 < (1ll << 32) && wrows * g.K * 2 < (1ll << 32);
+}
+
+template <bool SWIGLU>
+static void launch_tiled4_impl(const GroupedGemm& g, hipStream_t s) {
+  using C = Tiled4<SWIGLU>;
+  const int nt = g.N / C::BNOUT;
+  const int groups = g.offsets ? g.G : 1;
+  const long long bound = ((long long)(g.total_rows + C::BM - 1) / C::BM + groups) * nt;
+  auto k = ffn_tiled4<SWIGLU>;
+  const int grid = resident_grid(reinterpret_cast<const void*>(k), C::NTHR, bound);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(C::NTHR), 0, s, g, nt);
+}
+
+void launch_tiled4(const GroupedGemm& g, bool swiglu, hipStream_t s) {
+  if (swiglu)
+    launch_tiled4_impl<true>(g, s);
+  else
+    launch_tiled4_impl<false>(g, s);
+}
+
+}  // namespace moe

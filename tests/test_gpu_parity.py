@@ -29,6 +29,18 @@ SMALL = {
     # decode-sized (T <= 16): the layer's two-launch routing front end
     "wide_k_decode": CFG["tiny"].with_(name="wide_k_decode", T=16, E=256, k=32, I=128, x_seed=16,
                                        family_seed=1099),
+    # many rows per expert with K >= 320: the one-wave-per-SIMD tiled GEMMs
+    # (GEMM1 K = 512: 8 steps; GEMM2 K = 384: 6 steps), ragged m-tiles
+    "tiled4": CFG["tiny"].with_(name="tiled4", T=600, H=512, E=8, k=2, I=384, x_seed=17,
+                                family_seed=1017),
+    # more tiles than resident blocks (GEMM1 ~400, GEMM2 ~320), so the DMA ring
+    # streams from one tile into the next; 16 and 10 K-steps (not multiples of
+    # the three stages)
+    "tiled4_stream": CFG["tiny"].with_(name="tiled4_stream", T=2500, H=1024, E=8, k=4, I=640,
+                                       x_seed=18, family_seed=1018),
+    # sigmoid gating with a shared expert (the ungathered row path of the same kernels)
+    "tiled4_hy3": CFG["hy3"].with_(name="tiled4_hy3", T=700, H=512, E=16, k=4, I=384, shared_I=384,
+                                   x_seed=19, family_seed=1019),
 }
 
 
@@ -187,12 +199,13 @@ def _ffn_check(name):
         assert_close_bf16(y_g[r0:r1], act_g[r0:r1] @ w2.T, ATOL, RTOL, f"{name} y expert {e}")
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_T1", "small_prefill", "small_hy3", "wide_k"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_T1", "small_prefill", "small_hy3", "wide_k", "tiled4",
+                                  "tiled4_stream", "tiled4_hy3"])
 def test_grouped_ffn_rows(name):
     _ffn_check(name)
 
 
-@pytest.mark.parametrize("name", ["small_hy3", "small_hy3_decode"])
+@pytest.mark.parametrize("name", ["small_hy3", "small_hy3_decode", "tiled4_hy3"])
 def test_shared_ffn(name):
     L = get_layer(SMALL[name])
     _, _, sy = B.shared_ffn(L.weights, L.dev["x"])
@@ -225,7 +238,7 @@ def _layer_check(cfg, tokens=None):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_T1", "small_prefill", "small_hy3", "small_hy3_decode", "wide_k",
-                                  "wide_k_decode"])
+                                  "wide_k_decode", "tiled4", "tiled4_stream", "tiled4_hy3"])
 def test_layer_small(name):
     _layer_check(SMALL[name])
 
