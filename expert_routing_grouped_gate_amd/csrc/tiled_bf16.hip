@@ -4,9 +4,9 @@
 // [Qwen3] "GMM enablement and routing optimisation": one grouped matmul over
 // all experts; "MoE TP optimisation -> compute decomposition": w13 = gate
 // rows then up rows, SwiGLU = SiLU(first half) * second half, fused into the
-// GEMM1 epilogue.  Same arithmetic as the 8-wave tiled kernels of
-// ffn_bf16.hip (identical accumulation order, so identical results); only the
-// data movement and the schedule differ.
+// GEMM1 epilogue.  Same accumulation order as the 8-wave tiled kernels of
+// ffn_bf16.hip; SiLU from the hardware exp2 and reciprocal (about an ulp of
+// fp32 each, far below the bf16 rounding of the output).
 //
 // Block tile: BM = 128 activation rows x BN = 256 weight rows (GEMM1: the 128
 // gate rows n0.. and the matching 128 up rows, 128 output columns; GEMM2: 256
@@ -58,7 +58,11 @@ struct Frags {
   u32x4 b[NT];
 };
 
-template <bool SWIGLU>
+// GATHER (uniform for a launch, a template parameter so that the two row
+// paths never merge: a register loaded on one path and moved on the other
+// made the compiler drain every load before the move): activation row of
+// sorted row r is the token of pair sorted_pair[r], else r itself.
+template <bool SWIGLU, bool GATHER>
 __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles) {
   using C = Tiled4<SWIGLU>;
   constexpr int MT = C::MT, NT = C::NT, NW = C::NW;
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   const int li = lane & 15, kc = lane >> 4;
   const int K = g.K, nk = K / 64;  // nk >= 5 (launcher)
   const uint32_t rowb = 2u * (uint32_t)K;  // bytes per row
-  const int arows_total = g.gather ? g.total_rows / g.topk : g.total_rows;
+  const int arows_total = GATHER ? g.total_rows / g.topk : g.total_rows;
   const __amdgpu_buffer_rsrc_t ar = mx_rsrc(g.A, (uint32_t)arows_total * rowb);
   const uint32_t wrows = SWIGLU ? 2u * (uint32_t)g.up_off : (uint32_t)g.N;
   const uint32_t wbytes = wrows * rowb;
@@ -132,23 +136,25 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   // used right after its load: gather_issue loads the pair ids (rows past the
   // tile end reuse a valid row), gather_finish turns them into byte offsets
   // of the rows' step-0 chunk (pair ids clamped into the token range).
-  auto gather_issue = [&](const T4Tile& ti, int* raw) {
-    int r[C::LPA];
+  auto tile_rows = [&](const T4Tile& ti, int* r) {
 #pragma unroll
     for (int i = 0; i < C::LPA; ++i) r[i] = ti.row0 + min(8 * (wave + NW * i) + (lane >> 3), ti.nrows - 1);
-    if (g.gather) {
+  };
+  auto gather_issue = [&](const T4Tile& ti, int* raw) {
+    if (GATHER) {
+      int r[C::LPA];
+      tile_rows(ti, r);
 #pragma unroll
       for (int i = 0; i < C::LPA; ++i) raw[i] = g.sorted_pair[r[i]];
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::LPA; ++i) raw[i] = r[i];
     }
   };
-  auto gather_finish = [&](const int* raw, uint32_t* adma) {
+  auto gather_finish = [&](const T4Tile& ti, const int* raw, uint32_t* adma) {
+    int r[C::LPA];
+    tile_rows(ti, r);
 #pragma unroll
     for (int i = 0; i < C::LPA; ++i) {
-      const uint32_t arow = g.gather ? (uint32_t)min(max(raw[i], 0) / g.topk, arows_total - 1)
-                                     : (uint32_t)raw[i];
+      const uint32_t arow = GATHER ? (uint32_t)min(max(raw[i], 0) / g.topk, arows_total - 1)
+                                   : (uint32_t)r[i];
       adma[i] = arow * rowb + dchunk;
     }
   };
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
 
   T4Tile cur = locate(t), nxt = cur;
   uint32_t cur_adma[C::LPA], nxt_adma[C::LPA];
-  int nxt_raw[C::LPA];
+  int nxt_raw[C::LPA] = {};
   Frags<MT, NT> f0, f1;
   int buf = 0;  // stage of the current step (global step % 3)
 
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
 
   // first tile: its rows, then stages 0..2, then stage 0's first half
   gather_issue(cur, nxt_raw);
-  gather_finish(nxt_raw, cur_adma);
+  gather_finish(cur, nxt_raw, cur_adma);
 #pragma unroll
   for (int p = 0; p < C::NS; ++p) issue(cur, cur_adma, p, p);
   wait_vm<(C::NS - 1) * C::LPW>();
@@ -283,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
     // compiler's own wait for them (where paths merge) does not drain the ring.
 #pragma unroll
     for (int i = 0; i < C::LPA; ++i) asm volatile("" : "+v"(nxt_raw[i]));
-    gather_finish(nxt_raw, nxt_adma);
+    gather_finish(nxt, nxt_raw, nxt_adma);
     for (int kt = 2; kt < nk - 3; ++kt) step(acc, cur, cur_adma, kt + 3);
     // the last three steps stream in the next tile's first three
     step(acc, nxt, nxt_adma, 0);
@@ -309,8 +315,8 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
           for (int ni = 0; ni < NT / 2; ++ni) {
             const f32x4 gt = acc[mi][ni], up = acc[mi][ni + NT / 2];
             u32x2 pk;
-            pk.x = pack_bf16x2(gt[0] / (1.f + expf(-gt[0])) * up[0], gt[1] / (1.f + expf(-gt[1])) * up[1]);
-            pk.y = pack_bf16x2(gt[2] / (1.f + expf(-gt[2])) * up[2], gt[3] / (1.f + expf(-gt[3])) * up[3]);
+            pk.x = pack_bf16x2(silu_fast(gt[0]) * up[0], silu_fast(gt[1]) * up[1]);
+            pk.y = pack_bf16x2(silu_fast(gt[2]) * up[2], silu_fast(gt[3]) * up[3]);
             *reinterpret_cast<u32x2*>(orow + 64 * wn + 16 * ni) = pk;
           }
         } else {
@@ -345,22 +351,22 @@ bool tiled4_fits(const GroupedGemm& g, bool swiglu) {
          arows * g.K * 2 < (1ll << 32) && wrows * g.K * 2 < (1ll << 32);
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool GATHER>
 static void launch_tiled4_impl(const GroupedGemm& g, hipStream_t s) {
   using C = Tiled4<SWIGLU>;
   const int nt = g.N / C::BNOUT;
   const int groups = g.offsets ? g.G : 1;
   const long long bound = ((long long)(g.total_rows + C::BM - 1) / C::BM + groups) * nt;
-  auto k = ffn_tiled4<SWIGLU>;
+  auto k = ffn_tiled4<SWIGLU, GATHER>;
   const int grid = resident_grid(reinterpret_cast<const void*>(k), C::NTHR, bound);
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::NTHR), 0, s, g, nt);
 }
 
 void launch_tiled4(const GroupedGemm& g, bool swiglu, hipStream_t s) {
   if (swiglu)
-    launch_tiled4_impl<true>(g, s);
+    g.gather ? launch_tiled4_impl<true, true>(g, s) : launch_tiled4_impl<true, false>(g, s);
   else
-    launch_tiled4_impl<false>(g, s);
+    g.gather ? launch_tiled4_impl<false, true>(g, s) : launch_tiled4_impl<false, false>(g, s);
 }
 
 }  // namespace moe
