@@ -8,7 +8,8 @@ headers, helpers, tables or constants).
 
 The oracle is plain numpy in fp64: slow, step by step, in the order the
 pages describe the method, so that each function can be checked against its
-passage by eye.  See ``moe.py`` (gate, routing, expert FFN, combine, layer)
-and ``mx.py`` (the MX element and scale codecs).
+passage by eye.  See ``moe.py`` (gate, routing, expert FFN, combine, layer),
+``mx.py`` (the MX element and scale codecs) and ``norm.py`` (the residual add
++ RMSNorm before the layer).
 """
-from . import mx, moe  # noqa: F401
+from . import mx, moe, norm  # noqa: F401
