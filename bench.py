@@ -235,6 +235,75 @@ def cpu_baseline(cfg, cpu, budget_s):
                       f"(fp64 numpy; routing over all tokens each call), {dt:.1f} s"}
 
 
+NORM_CONFIGS = {
+    # the norm before the MoE layer at the prefill shape: "RMSNorm + Cast"
+    # (fp32 for the gate, bf16 for the experts, the residual) and "RMSNorm +
+    # MX quant" (MXFP8 codes and scales, the residual)
+    "add_rmsnorm": dict(T=4096, H=4096, mx=False),
+    "add_rmsnorm_mx": dict(T=4096, H=4096, mx=True),
+}
+
+
+def bench_norm(args):
+    """The residual add + RMSNorm step (moe_add_rmsnorm) alone: one step =
+    one call over T tokens, inputs resident in HBM; HIP events (torch's, on
+    the stream the binding launches on) around every timed call."""
+    import numpy as np
+    import torch
+
+    from expert_routing_grouped_gate_amd import binding as B
+    from expert_routing_grouped_gate_amd import workloads as W
+
+    c = NORM_CONFIGS[args.config]
+    T, H, use_mx = c["T"], c["H"], c["mx"]
+    eps = 1e-6
+    x, r, w = W.draw_norm_inputs(T, H, seed=4096)
+    xd, rd, wd = x.cuda(), r.cuda(), w.cuda()
+    kw = dict(f32=not use_mx, bf16=not use_mx, residual_out=True, mx=use_mx)
+    for _ in range(args.warmup):
+        B.add_rmsnorm(xd, wd, eps, rd, **kw)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        B.add_rmsnorm(xd, wd, eps, rd, **kw)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    k_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    out_b = (1 + 1 / 32 + 2) if use_mx else (4 + 2 + 2)
+    alg = int(2 * T * H * 2 + H * 2 + out_b * T * H)
+    gbs = alg / (k_ms * 1e-3) / 1e9
+    cpu_b = None
+    if not args.no_cpu_baseline:
+        from oracle import norm
+        import threadpoolctl
+        xs, rs, ws = x.double().numpy(), r.double().numpy(), w.double().numpy()
+        n, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < min(args.cpu_budget_s, 5.0):
+            norm.add_rmsnorm(xs, rs, ws, eps)
+            n += 1
+        dt = time.perf_counter() - t1
+        blas = [i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        cpu_b = {"value": round(n * T / dt, 1), "unit": "tokens/s", "cores": max([1] + blas), "kind": "oracle",
+                 "sample": f"{n} oracle calls over all {T} tokens (fp64 numpy), {dt:.1f} s"}
+    form = "MXFP8 codes + scales and bf16 residual" if use_mx else "fp32 + bf16 outputs and bf16 residual"
+    res = {
+        "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.config}: residual add + RMSNorm before the MoE layer, T={T} H={H}, {form}",
+                   "T": T, "H": H, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "add_rmsnorm_kernel",
+                     "kernel_ms": round(k_ms, 5), "algorithmic_bytes": alg},
+        "cpu_baseline": cpu_b,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -255,6 +324,9 @@ def main():
         calibrate_copy(args.calibrate_copy_mib)
         return
     B.load()
+    if args.config in NORM_CONFIGS:
+        bench_norm(args)
+        return
     cfg = W.CONFIGS[args.config]
     log(f"[bench] drawing {cfg.name}")
     cpu = W.draw_layer(cfg, progress=log)

@@ -66,6 +66,7 @@ SIGNATURES = {
     "moe_route_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_route": (_I, [_vp, _I, _I, _I, _vp, _vp, _vp, _vp, _vp, _vp, _SZ, _vp]),
     "moe_mx_quantize": (_I, [_vp, _I, _I, _vp, _vp, _vp]),
+    "moe_add_rmsnorm": (_I, [_vp, _vp, _vp, _I, _I, _F, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_mx_packed_scales_bytes": (_SZ, [_I, _I]),
     "moe_mx_pack_weight": (_I, [_vp, _vp, _I, _I, _I, _vp, _vp, _vp]),
     "moe_grouped_ffn_up": (_I, [_P(MoeFfnWeights), _vp, _vp, _I, _I, _vp, _vp, _vp, _vp, _vp]),
@@ -187,6 +188,34 @@ def mx_quantize(x: torch.Tensor):
     scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
     _check("moe_mx_quantize", load().moe_mx_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
+
+
+def add_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, residual: Optional[torch.Tensor] = None,
+                f32: bool = True, bf16: bool = True, residual_out: bool = True, mx: bool = False):
+    """moe_add_rmsnorm: residual add + RMSNorm.  Returns a dict with the
+    requested outputs: "f32" [T, H] fp32, "bf16" [T, H] bf16, "residual"
+    [T, H] bf16, "mx" ([T, H] uint8 codes, [T, H/32] uint8 scales)."""
+    _dev(x, weight, *(() if residual is None else (residual,)))
+    assert x.dtype == torch.bfloat16 and weight.dtype == torch.bfloat16
+    T, H = x.shape
+    assert weight.shape == (H,) and (residual is None or (residual.shape == (T, H) and residual.dtype == torch.bfloat16))
+    out = {}
+    if f32:
+        out["f32"] = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if bf16:
+        out["bf16"] = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if residual_out:
+        out["residual"] = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    if mx:
+        out["mx"] = (torch.empty((T, H), dtype=torch.uint8, device=x.device),
+                     torch.empty((T, H // 32), dtype=torch.uint8, device=x.device))
+    p = lambda k: _ptr(out[k]) if k in out else None  # noqa: E731
+    q, qs = out.get("mx", (None, None))
+    _check("moe_add_rmsnorm", load().moe_add_rmsnorm(
+        _ptr(x), None if residual is None else _ptr(residual), _ptr(weight), T, H, float(eps),
+        p("f32"), p("bf16"), p("residual"), None if q is None else _ptr(q), None if qs is None else _ptr(qs),
+        _stream()))
+    return out
 
 
 def mx_pack_weight(codes: torch.Tensor, scales: torch.Tensor):

@@ -344,6 +344,22 @@ int moe_grouped_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scal
   return st;
 }
 
+int moe_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* weight, int T,
+                    int H, float eps, float* y_f32, uint16_t* y_bf16, uint16_t* residual_out,
+                    uint8_t* y_mx, uint8_t* y_mx_scales, void* stream) {
+  int st;
+  if (T < 0 || H <= 0) return MOE_ERR_SHAPE;
+  if (H % 32 != 0 || H > 16384) return MOE_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || eps == __builtin_inff()) return MOE_ERR_SHAPE;  // also rejects NaN
+  if (T == 0) return MOE_OK;
+  if ((y_mx == nullptr) != (y_mx_scales == nullptr)) return MOE_ERR_NULL;
+  if (!y_f32 && !y_bf16 && !residual_out && !y_mx) return MOE_ERR_NULL;
+  if ((st = check_ptrs({x, weight}))) return st;
+  if ((st = check_optional({residual, y_f32, y_bf16, residual_out, y_mx, y_mx_scales}))) return st;
+  return moe::launch_add_rmsnorm(x, residual, weight, T, H, eps, y_f32, y_bf16, residual_out, y_mx,
+                                 y_mx_scales, as_stream(stream));
+}
+
 int moe_combine(const uint16_t* y, const int32_t* pair_pos, const float* topk_w,
                 const uint16_t* shared_y, int T, int k, int H, uint16_t* out, void* stream) {
   int st;

@@ -83,6 +83,12 @@ size_t mx_packed_scales_bytes(int rows, int K);
 int launch_mx_pack(const uint8_t* codes, const uint8_t* scales, int G, int R, int K,
                    uint8_t* packed_codes, uint8_t* packed_scales, hipStream_t s);
 
+// Residual add + RMSNorm (T >= 1, H % 32 == 0, H <= 16384); any output may be
+// null (q and qs together).
+int launch_add_rmsnorm(const uint16_t* x, const uint16_t* res, const uint16_t* w, int T, int H,
+                       float eps, float* yf, uint16_t* yb, uint16_t* rout, uint8_t* q,
+                       uint8_t* qs, hipStream_t s);
+
 int launch_combine(const uint16_t* y, const int32_t* pair_pos, const float* w,
                    const uint16_t* shared_y, int T, int k, int H, uint16_t* out, hipStream_t s);
 

@@ -37,6 +37,7 @@ import torch
 # tensor tags used in seed derivation
 _TAG_X, _TAG_ROUTER, _TAG_BIAS, _TAG_W13, _TAG_W2, _TAG_SHARED = 1, 2, 3, 4, 5, 6
 _TAG_MX_W13, _TAG_MX_W2, _TAG_MX_SHARED = 7, 8, 9
+_TAG_NORM_X, _TAG_NORM_RES, _TAG_NORM_W = 10, 11, 12
 
 
 @dataclass(frozen=True)
@@ -238,3 +239,13 @@ def draw_layer(cfg: LayerConfig, progress=None) -> dict:
             (t["shared_w13"], t["shared_w13_scales"], t["shared_w2"],
              t["shared_w2_scales"]) = draw_shared_mx(cfg)
     return t
+
+
+def draw_norm_inputs(T: int, H: int, seed: int):
+    """Inputs of the residual add + RMSNorm before the layer: hidden states
+    x and residual [T, H] bf16 ~ N(0,1), and the norm weight [H] bf16 ~
+    N(1, 0.1) (RMSNorm weights start at one)."""
+    x = _normal((T, H), 1.0, seed, _TAG_NORM_X, T, H).to(torch.bfloat16)
+    r = _normal((T, H), 1.0, seed, _TAG_NORM_RES, T, H).to(torch.bfloat16)
+    w = (1.0 + _normal((H,), 0.1, seed, _TAG_NORM_W, H)).to(torch.bfloat16)
+    return x, r, w

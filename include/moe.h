@@ -130,6 +130,35 @@ int moe_route(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
               int32_t* dev_status, void* workspace, size_t workspace_bytes,
               void* stream);
 
+/* ----------------------------------------------- before the layer -----
+ * Residual add + RMSNorm in one pass, with the outputs the MoE layer takes
+ * ([Qwen3] "fused-operator optimisation": "fused RMSNorm + MX quant" and
+ * "fused RMSNorm + Cast" (FP32 for the gate, BF16 for the experts, plus the
+ * updated residual); the formula as written in the "LLM inference
+ * optimisation study note", section 2, "Add and RMSNorm").  Per row:
+ *   z = x + residual (x alone when residual is NULL), in fp32;
+ *   y_i = z_i / sqrt(mean_j z_j^2 + eps) * weight_i (sum of squares in
+ *   fp32, the reciprocal root in fp64, the products in fp32).
+ *   x            [T, H] bf16
+ *   residual     [T, H] bf16, or NULL (first layer)
+ *   weight       [H] bf16 (the norm's gamma)
+ *   eps          >= 0 and finite (variance epsilon)
+ * Outputs, each may be NULL (at least one must be given):
+ *   y_f32        [T, H] fp32: y (the gate's input)
+ *   y_bf16       [T, H] bf16: y rounded to nearest even (the experts' input)
+ *   residual_out [T, H] bf16: z rounded to nearest even (the next layer's
+ *                residual)
+ *   y_mx, y_mx_scales  [T, H] uint8 E4M3 codes + [T, H/32] uint8 E8M0 scales
+ *                of y quantised with the rule of moe_mx_quantize (both or
+ *                neither)
+ * No output may overlap an input.  Limits: H % 32 == 0, H <= 16384.  T == 0
+ * enqueues nothing.  Errors: MOE_ERR_NULL (x or weight NULL, no output, or
+ * only one of y_mx / y_mx_scales), MOE_ERR_SHAPE (T < 0, H <= 0, eps negative
+ * or not finite), MOE_ERR_UNSUPPORTED (H outside the limits), MOE_ERR_ALIGN. */
+int moe_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t* weight, int T,
+                    int H, float eps, float* y_f32, uint16_t* y_bf16, uint16_t* residual_out,
+                    uint8_t* y_mx, uint8_t* y_mx_scales, void* stream);
+
 /* ------------------------------------------------------------- S0 -----
  * Dynamic MXFP8 quantisation ([Qwen3] "MoE EP optimisation": hidden_states
  * -> MXFP8 data + scale; round_mode rint, dst_type float8_e4m3fn).  Per

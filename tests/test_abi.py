@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("moe_gate_topk", "moe_route", "moe_grouped_ffn", "moe_combine",
-                 "moe_layer_forward", "moe_router_logits", "moe_mx_quantize",
+                 "moe_layer_forward", "moe_router_logits", "moe_mx_quantize", "moe_add_rmsnorm",
                  "moe_status_string", "moe_layer_workspace_size"):
         assert want in names
     assert set(names) == set(B.SIGNATURES), "binding and header disagree"
@@ -121,6 +121,27 @@ def test_combine_checks(lib):
     assert f(FAKE, None, FAKE, None, 4, 2, 256, FAKE, None) == NULL
     assert f(FAKE, FAKE, FAKE, MIS, 4, 2, 256, FAKE, None) == ALIGN
     assert f(FAKE, FAKE, FAKE, None, 4, 33, 256, FAKE, None) == UNSUP
+
+
+def test_add_rmsnorm_checks(lib):
+    f = lib.moe_add_rmsnorm
+    args = lambda **kw: [kw.get(k, v) for k, v in (  # noqa: E731
+        ("x", FAKE), ("r", None), ("w", FAKE), ("T", 4), ("H", 256), ("eps", 1e-6), ("yf", FAKE),
+        ("yb", None), ("ro", None), ("q", None), ("qs", None), ("s", None))]
+    assert f(*args(H=100)) == UNSUP                     # H % 32
+    assert f(*args(H=16384 + 32)) == UNSUP
+    assert f(*args(H=0)) == SHAPE
+    assert f(*args(T=-1)) == SHAPE
+    assert f(*args(eps=-1.0)) == SHAPE
+    assert f(*args(eps=float("nan"))) == SHAPE
+    assert f(*args(eps=float("inf"))) == SHAPE
+    assert f(*args(yf=None)) == NULL                    # no output at all
+    assert f(*args(q=FAKE)) == NULL                     # codes without scales
+    assert f(*args(x=None)) == NULL
+    assert f(*args(w=None)) == NULL
+    assert f(*args(r=MIS)) == ALIGN
+    assert f(*args(yb=MIS)) == ALIGN
+    assert f(*args(T=0)) == OK                          # nothing to do, nothing enqueued
 
 
 def test_layer_forward_checks(lib):

@@ -1,0 +1,125 @@
+"""GPU parity of the residual add + RMSNorm before the layer
+(moe_add_rmsnorm) against the oracle (oracle/norm.py), through the C ABI.
+
+Bars: the residual output z rounded to bf16 is bit-exact (the fp32 sum of
+two bf16 values is exact); the fp32 output within 1e-5 relative (the
+kernel's fp32 sum of squares over at most 8 * ceil(H / 2048) + 8 sequential
+additions per path, a root in fp64 and two fp32 products stay below 1e-6);
+the bf16 output is the round-to-nearest-even of the kernel's own fp32 output
+and within one bf16 step of the oracle's; the MXFP8 codes and scales equal
+the oracle's quantiser applied to the kernel's fp32 output (the block
+exponent is an integer decided in the kernel's precision)."""
+import numpy as np
+import pytest
+import torch
+
+from expert_routing_grouped_gate_amd import binding as B
+from expert_routing_grouped_gate_amd import workloads as W
+from oracle import mx, norm
+
+pytestmark = pytest.mark.gpu
+
+RTOL_F32 = 1e-5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    B.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _bf16_step(v):
+    """Distance between neighbouring bf16 values around |v| (v > 0 normal)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+# (T, H): one 32-block; 12 chunks; the decode and prefill hidden size; a
+# width that leaves some threads with one chunk fewer; the largest width
+CASES = [(1, 32), (7, 96), (16, 4096), (333, 4096), (5, 2080), (64, 16384)]
+
+
+@pytest.mark.parametrize("with_residual", [True, False])
+@pytest.mark.parametrize("T,H", CASES)
+def test_add_rmsnorm_parity(T, H, with_residual):
+    eps = 1e-6
+    x, r, w = W.draw_norm_inputs(T, H, seed=100 + T + H)
+    res = r if with_residual else None
+    out = B.add_rmsnorm(x.cuda(), w.cuda(), eps, None if res is None else res.cuda(), mx=True)
+    torch.cuda.synchronize()
+    z, y = norm.add_rmsnorm(x.double().numpy(), None if res is None else res.double().numpy(),
+                            w.double().numpy(), eps)
+    # residual: bit-exact
+    np.testing.assert_array_equal(out["residual"].double().cpu().numpy(), mx.bf16_round(z))
+    # fp32 y
+    yf = out["f32"].double().cpu().numpy()
+    err = np.abs(yf - y)
+    assert np.all(err <= RTOL_F32 * np.abs(y)), f"max rel err {np.max(err / np.maximum(np.abs(y), 1e-30))}"
+    # bf16 y: RNE of the kernel's fp32 y, one bf16 step from the oracle's
+    yb = out["bf16"].double().cpu().numpy()
+    np.testing.assert_array_equal(yb, mx.bf16_round(yf))
+    assert np.all(np.abs(yb - mx.bf16_round(y)) <= _bf16_step(y))
+    # MXFP8: the oracle's quantiser on the kernel's fp32 y, bit for bit
+    codes, scales = mx.mxfp8_quantize(yf)
+    np.testing.assert_array_equal(out["mx"][0].cpu().numpy(), codes)
+    np.testing.assert_array_equal(out["mx"][1].cpu().numpy(), scales)
+    # and against the exact y the scales agree except where a block's amax
+    # sits within the fp32 error of a power of two
+    _, s_exact = mx.mxfp8_quantize(y)
+    assert np.mean(s_exact == scales) > 0.999
+
+
+def test_each_output_alone_equals_all_together():
+    T, H = 40, 4096
+    x, r, w = (t.cuda() for t in W.draw_norm_inputs(T, H, seed=7))
+    full = B.add_rmsnorm(x, w, 1e-5, r, mx=True)
+    only_bf16 = B.add_rmsnorm(x, w, 1e-5, r, f32=False, residual_out=False)
+    only_res = B.add_rmsnorm(x, w, 1e-5, r, f32=False, bf16=False)
+    only_mx = B.add_rmsnorm(x, w, 1e-5, r, f32=False, bf16=False, residual_out=False, mx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(full["bf16"], only_bf16["bf16"])
+    assert torch.equal(full["residual"], only_res["residual"])
+    assert torch.equal(full["mx"][0], only_mx["mx"][0]) and torch.equal(full["mx"][1], only_mx["mx"][1])
+
+
+def test_zero_row_and_large_eps():
+    """A zero row normalises to zeros (eps > 0); a large eps shrinks y by
+    sqrt(ms / (ms + eps))."""
+    T, H = 3, 256
+    x, r, w = W.draw_norm_inputs(T, H, seed=9)
+    x[1] = 0
+    r[1] = 0
+    for eps in (1e-6, 4.0):
+        out = B.add_rmsnorm(x.cuda(), w.cuda(), eps, r.cuda())
+        torch.cuda.synchronize()
+        _, y = norm.add_rmsnorm(x.double().numpy(), r.double().numpy(), w.double().numpy(), eps)
+        yf = out["f32"].double().cpu().numpy()
+        assert np.all(yf[1] == 0.0)
+        assert np.all(np.abs(yf - y) <= RTOL_F32 * np.abs(y))
+
+
+def test_zero_tokens():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(256, dtype=torch.bfloat16, device="cuda")
+    out = B.add_rmsnorm(x, w, 1e-6)
+    assert out["f32"].shape == (0, 256)
+
+
+def test_mx_output_dequantises_to_y():
+    """The MXFP8 output dequantises to the fp32 output within the format's
+    bound: half an E4M3 step (2^-4 of the element, or 2^-10 of the block
+    scale in the subnormal range); elements beyond 448 x scale (the rule
+    saturates scaled values in [448, 512)) lose exactly the clipped part."""
+    T, H = 16, 4096
+    x, r, w = (t.cuda() for t in W.draw_norm_inputs(T, H, seed=21))
+    out = B.add_rmsnorm(x, w, 1e-6, r, mx=True)
+    torch.cuda.synchronize()
+    yf = out["f32"].double().cpu().numpy()
+    deq = mx.mxfp8_dequant(out["mx"][0].cpu().numpy(), out["mx"][1].cpu().numpy())
+    scale = np.repeat(mx.e8m0_decode(out["mx"][1].cpu().numpy()), 32, axis=-1)
+    sat = np.abs(yf) > 448 * scale
+    bound = np.where(sat, np.abs(yf) - 448 * scale, np.maximum(2.0 ** -4 * np.abs(yf), 2.0 ** -10 * scale))
+    assert np.all(np.abs(deq - yf) <= bound * (1 + 1e-12))
+    assert np.all(np.abs(deq[sat]) == 448 * scale[sat])
