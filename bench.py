@@ -73,12 +73,20 @@ class TimingEvent:
             hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                 ctypes.c_void_p]
             hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             TimingEvent._hip = hip
         h = ctypes.c_void_p()
         rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE)
         if rc != 0:
             raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
         self.cuda_event = h.value   # the handle MoeLayer.time_ffn_up passes to the library
+
+    def record(self, stream_handle) -> None:
+        """Record on a stream (a hipStream_t handle, e.g. torch's
+        current_stream().cuda_stream)."""
+        rc = TimingEvent._hip.hipEventRecord(self.cuda_event, stream_handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, end: "TimingEvent") -> float:
         import ctypes
@@ -121,10 +129,10 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     sf, sw = kib / cf, kib / cw
     lines = [f"# HBM byte counters, Qwen3-style decode layer (T=16, H=4096, E=128, top-8, I=1536, bf16)", "",
              "Each counter in its own pass (run from /tmp on one MI355X, repo at $R):", "", "```",
-             "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_fetch_decode -o run --output-format csv -- python $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
-             "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_write_decode -o run --output-format csv -- python $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
-             "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_fetch_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
-             "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_write_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
+             "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE_decode -o run --output-format csv -- python $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_WRITE_SIZE_decode -o run --output-format csv -- python $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
+             "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_WRITE_SIZE_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
              "python $R/bench.py --summarize-counters <the four run_counter_collection.csv files>", "```", "",
              f"Calibration (1 GiB device copy): FETCH_SIZE {cf:,.1f} KiB -> scale x{sf:.3f}; "
              f"WRITE_SIZE {cw:,.1f} KiB -> scale x{sw:.3f}.", "",
@@ -246,8 +254,9 @@ NORM_CONFIGS = {
 
 def bench_norm(args):
     """The residual add + RMSNorm step (moe_add_rmsnorm) alone: one step =
-    one call over T tokens, inputs resident in HBM; HIP events (torch's, on
-    the stream the binding launches on) around every timed call."""
+    one call over T tokens, inputs resident in HBM; fence-free HIP events on
+    the stream the binding launches on (torch's current stream) around every
+    timed call."""
     import numpy as np
     import torch
 
@@ -264,15 +273,16 @@ def bench_norm(args):
         B.add_rmsnorm(xd, wd, eps, rd, **kw)
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(K)]
+    stream = torch.cuda.current_stream().cuda_stream
     t0 = time.perf_counter()
     for i in range(K):
-        ev[i][0].record()
+        ev[i][0].record(stream)
         B.add_rmsnorm(xd, wd, eps, rd, **kw)
-        ev[i][1].record()
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / K
-    k_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    k_ms = sum(a.elapsed_ms(b) for a, b in ev) / K
     out_b = (1 + 1 / 32 + 2) if use_mx else (4 + 2 + 2)
     alg = int(2 * T * H * 2 + H * 2 + out_b * T * H)
     gbs = alg / (k_ms * 1e-3) / 1e9
