@@ -67,6 +67,8 @@ SIGNATURES = {
     "moe_route": (_I, [_vp, _I, _I, _I, _vp, _vp, _vp, _vp, _vp, _vp, _SZ, _vp]),
     "moe_mx_quantize": (_I, [_vp, _I, _I, _vp, _vp, _vp]),
     "moe_add_rmsnorm": (_I, [_vp, _vp, _vp, _I, _I, _F, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_router_f32_workspace_size": (_SZ, [_I, _I, _I]),
+    "moe_router_logits_f32": (_I, [_vp, _vp, _I, _I, _I, _vp, _vp, _SZ, _vp]),
     "moe_mx_packed_scales_bytes": (_SZ, [_I, _I]),
     "moe_mx_pack_weight": (_I, [_vp, _vp, _I, _I, _I, _vp, _vp, _vp]),
     "moe_grouped_ffn_up": (_I, [_P(MoeFfnWeights), _vp, _vp, _I, _I, _vp, _vp, _vp, _vp, _vp]),
@@ -188,6 +190,22 @@ def mx_quantize(x: torch.Tensor):
     scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
     _check("moe_mx_quantize", load().moe_mx_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
+
+
+def router_logits_f32(x: torch.Tensor, wr: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """moe_router_logits_f32: logits [T, E] fp32 from fp32 hidden states."""
+    _dev(x, wr)
+    assert x.dtype == torch.float32 and wr.dtype == torch.float32
+    T, H = x.shape
+    E = wr.shape[0]
+    lib = load()
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    nbytes = lib.moe_router_f32_workspace_size(T, H, E)
+    ws = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=x.device)
+    _check("moe_router_logits_f32", lib.moe_router_logits_f32(_ptr(x), _ptr(wr), T, H, E, _ptr(out), _ptr(ws),
+                                                            ws.numel(), _stream()))
+    return out
 
 
 def add_rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, residual: Optional[torch.Tensor] = None,

@@ -159,6 +159,26 @@ int moe_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, f
                                    as_stream(stream));
 }
 
+size_t moe_router_f32_workspace_size(int T, int H, int E) {
+  if (T <= 0 || check_dims_HE(H, E) != MOE_OK) return 0;
+  return moe::router_f32_workspace_bytes(T, H, E);
+}
+
+int moe_router_logits_f32(const float* x, const float* wr, int T, int H, int E, float* logits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  int st;
+  if ((st = check_dims_HE(H, E))) return st;
+  if (T < 0) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if ((long long)T * E >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_ptrs({x, wr, logits}))) return st;
+  const size_t need = moe::router_f32_workspace_bytes(T, H, E);
+  if (workspace == nullptr || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!al16(workspace)) return MOE_ERR_ALIGN;
+  return moe::launch_router_logits_f32(x, wr, T, H, E, logits, static_cast<float*>(workspace),
+                                       as_stream(stream));
+}
+
 int moe_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,
                   float routed_scale, float eps, int32_t* topk_ids, float* topk_w,
                   void* stream) {

@@ -252,6 +252,92 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
   }
 }
 
+// ------------------------------------------------ S1, fp32 hidden states ---
+// The gate's input is fp32 ([Qwen3] "fused RMSNorm + Cast": the norm before
+// the MoE block hands the gate an FP32 copy of the hidden states).  Block
+// (token tile, expert tile, 256-column slice s of H): 64 tokens x 64 experts,
+// partial[s][t][e] = sum over the slice of x[t][h] * Wr[e][h] with fp64
+// accumulation (each product of two fp32 values is exact in fp64), rounded to
+// fp32 once; router_reduce then sums the slices in order.  Operands are staged
+// in LDS transposed (k-major), so a thread's 4 tokens and 4 experts at one k
+// are two 16-byte reads; thread (ty, tx) owns tokens 4 ty.. and experts 4 tx...
+constexpr int RF_T = 64, RF_E = 64, RF_K = 64;
+
+__global__ __launch_bounds__(256) void router_partial_f32(const float* __restrict__ x,
+                                                          const float* __restrict__ wr, int T,
+                                                          int H, int E,
+                                                          float* __restrict__ partial) {
+  __shared__ float xs[RF_K][RF_T];
+  __shared__ float ws[RF_K][RF_E];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * RF_T, e0 = blockIdx.y * RF_E, h0 = blockIdx.z * RP_HS;
+  const int ty = tid >> 4, tx = tid & 15;
+  // loader: row (token or expert) tid / 4, 16 consecutive k at 16 * (tid % 4)
+  const int lr = tid >> 2, lk = 16 * (tid & 3);
+  const float* xrow = x + (size_t)min(t0 + lr, T - 1) * H + h0 + lk;  // rows past T reuse a valid row
+  const float* wrow = wr + (size_t)min(e0 + lr, E - 1) * H + h0 + lk;
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+  for (int kc = 0; kc < RP_HS; kc += RF_K) {
+    f32x4 xv[4], wv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      xv[q] = *reinterpret_cast<const f32x4*>(xrow + kc + 4 * q);
+      wv[q] = *reinterpret_cast<const f32x4*>(wrow + kc + 4 * q);
+    }
+    __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xs[lk + 4 * q + i][lr] = xv[q][i];
+        ws[lk + 4 * q + i][lr] = wv[q][i];
+      }
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < RF_K; ++k) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&xs[k][4 * ty]);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(&ws[k][4 * tx]);
+      double bd[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bd[j] = (double)b[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double ad = (double)a[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fma(ad, bd[j], acc[i][j]);
+      }
+    }
+  }
+  float* out = partial + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * ty + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + 4 * tx + j;
+      if (e < E) out[(size_t)t * E + e] = (float)acc[i][j];
+    }
+  }
+}
+
+size_t router_f32_workspace_bytes(int T, int H, int E) {
+  return (size_t)(H / RP_HS) * (size_t)T * (size_t)E * sizeof(float);
+}
+
+int launch_router_logits_f32(const float* x, const float* wr, int T, int H, int E, float* logits,
+                             float* ws, hipStream_t s) {
+  hipLaunchKernelGGL(router_partial_f32, dim3((T + RF_T - 1) / RF_T, (E + RF_E - 1) / RF_E, H / RP_HS),
+                     dim3(256), 0, s, x, wr, T, H, E, ws);
+  hipLaunchKernelGGL(router_reduce, dim3((T * E + 255) / 256), dim3(256), 0, s, ws, H / RP_HS, T,
+                     E, logits);
+  return launch_status();
+}
+
 int launch_router_partial(const uint16_t* x, const float* wr, int T, int H, int E,
                           float* partial, uint8_t* xq, uint8_t* xq_scales, hipStream_t s) {
   hipLaunchKernelGGL(router_partial, dim3((E + 15) / 16, H / RP_HS, (T + 15) / 16), dim3(64), 0,

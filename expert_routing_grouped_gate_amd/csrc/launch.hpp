@@ -22,6 +22,11 @@ int resident_grid(const void* kernel, int block, long long max_tiles);
 size_t router_workspace_bytes(int T, int H, int E);
 int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
                          float* ws, hipStream_t s);
+// Router logits from fp32 hidden states (any T): split-H partials with fp64
+// accumulation, summed in slice order; workspace [H/256, T, E] fp32.
+size_t router_f32_workspace_bytes(int T, int H, int E);
+int launch_router_logits_f32(const float* x, const float* wr, int T, int H, int E, float* logits,
+                             float* ws, hipStream_t s);
 // Few-token layer front end: partial logits (+ MXFP8 x when xq != nullptr),
 // then one block for logits, top-k, counts and the permutation (T <= 16,
 // T*k <= 1024).

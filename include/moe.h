@@ -90,6 +90,23 @@ size_t moe_router_workspace_size(int T, int H, int E);
 int moe_router_logits(const uint16_t* x, const float* wr, int T, int H, int E,
                       float* logits, void* workspace, size_t workspace_bytes, void* stream);
 
+/* S1 from fp32 hidden states ([Qwen3] "fused RMSNorm + Cast": the norm before
+ * the MoE block gives the gate an FP32 copy of the hidden states, e.g. the
+ * y_f32 output of moe_add_rmsnorm).  L[t, e] = sum_h x[t, h] * wr[e, h]; the
+ * products and their sums over each 256-column slice of H are taken in
+ * fp64 and rounded to fp32 once, the slices are then added in order in fp32.
+ *   x      [T, H] fp32
+ *   wr     [E, H] fp32
+ *   logits [T, E] fp32 (output)
+ *   workspace  device scratch of moe_router_f32_workspace_size(T, H, E) bytes
+ *              (the per-slice sums, [H/256, T, E] fp32); MOE_ERR_WORKSPACE when
+ *              missing or too small.
+ * Limits as moe_router_logits (H % 256 == 0, E <= 256), T * E < 2^31.
+ * Deterministic: the summation order of each output is fixed. */
+size_t moe_router_f32_workspace_size(int T, int H, int E);
+int moe_router_logits_f32(const float* x, const float* wr, int T, int H, int E, float* logits,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------- S2 -----
  * Gate top-k ([Qwen3] gating top-k softmax; [Hy3] section 1.3 router call
  * with k, bias, sigmoid norm type, routed_scaling_factor and eps).

@@ -123,6 +123,22 @@ def test_combine_checks(lib):
     assert f(FAKE, FAKE, FAKE, None, 4, 33, 256, FAKE, None) == UNSUP
 
 
+def test_router_logits_f32_checks(lib):
+    f = lib.moe_router_logits_f32
+    ws = lib.moe_router_f32_workspace_size(4, 512, 8)
+    assert ws == 2 * 4 * 8 * 4                                   # two 256-wide slices of partials
+    assert lib.moe_router_f32_workspace_size(0, 512, 8) == 0
+    assert lib.moe_router_f32_workspace_size(4, 500, 8) == 0
+    assert f(FAKE, FAKE, 4, 500, 8, FAKE, FAKE, ws, None) == UNSUP   # H % 256
+    assert f(FAKE, FAKE, 4, 512, 257, FAKE, FAKE, ws, None) == UNSUP
+    assert f(FAKE, FAKE, -1, 512, 8, FAKE, FAKE, ws, None) == SHAPE
+    assert f(None, FAKE, 4, 512, 8, FAKE, FAKE, ws, None) == NULL
+    assert f(FAKE, FAKE, 4, 512, 8, FAKE, None, ws, None) == WS
+    assert f(FAKE, FAKE, 4, 512, 8, FAKE, FAKE, ws - 4, None) == WS
+    assert f(FAKE, FAKE, 4, 512, 8, FAKE, MIS, ws, None) == ALIGN
+    assert f(FAKE, FAKE, 0, 512, 8, FAKE, None, 0, None) == OK
+
+
 def test_add_rmsnorm_checks(lib):
     f = lib.moe_add_rmsnorm
     args = lambda **kw: [kw.get(k, v) for k, v in (  # noqa: E731

@@ -123,3 +123,55 @@ def test_mx_output_dequantises_to_y():
     bound = np.where(sat, np.abs(yf) - 448 * scale, np.maximum(2.0 ** -4 * np.abs(yf), 2.0 ** -10 * scale))
     assert np.all(np.abs(deq - yf) <= bound * (1 + 1e-12))
     assert np.all(np.abs(deq[sat]) == 448 * scale[sat])
+
+
+# ------------------------------------------- the gate's fp32 input: S1 ----
+# moe_router_logits_f32: products and per-slice sums in fp64, 16 slice sums
+# (H = 4096) rounded to fp32 and added in fp32: at most ~20 fp32 roundings of
+# values of the logits' size (|L| < 3 here), so 2e-5 is a tenfold margin.
+ATOL_LOGITS = 2e-5
+
+
+@pytest.mark.parametrize("T,H,E", [(1, 256, 8), (16, 4096, 128), (333, 4096, 192), (70, 512, 256),
+                                   (4096, 4096, 128)])
+def test_router_logits_f32(T, H, E):
+    g = torch.Generator().manual_seed(T * 7 + H + E)
+    x = torch.randn((T, H), generator=g, dtype=torch.float32)
+    wr = torch.randn((E, H), generator=g, dtype=torch.float32) * 0.02
+    got = B.router_logits_f32(x.cuda(), wr.cuda())
+    torch.cuda.synchronize()
+    ref = x.double().numpy() @ wr.double().numpy().T
+    np.testing.assert_allclose(got.double().cpu().numpy(), ref, atol=ATOL_LOGITS, rtol=0)
+
+
+def test_router_logits_f32_exact_on_small_integers():
+    """Integer inputs whose every partial sum is an integer below 2^24: the
+    logits are exact."""
+    g = torch.Generator().manual_seed(5)
+    x = torch.randint(-4, 5, (40, 1024), generator=g).float()
+    wr = torch.randint(-3, 4, (24, 1024), generator=g).float()
+    got = B.router_logits_f32(x.cuda(), wr.cuda())
+    torch.cuda.synchronize()
+    want = (x.double() @ wr.double().T).numpy()
+    np.testing.assert_array_equal(got.double().cpu().numpy(), want)
+
+
+def test_norm_feeds_the_gate_in_fp32():
+    """The step before the layer and the layer's S1/S2 chained on the device:
+    add + RMSNorm -> fp32 y -> router logits -> top-k.  Logits against the
+    oracle's fp64 logits of the same fp32 y; the selection against the
+    oracle's gate on the GPU's logits (ids bit-exact)."""
+    from oracle import moe
+    T, H, E, k = 64, 4096, 128, 8
+    x, r, w = (t.cuda() for t in W.draw_norm_inputs(T, H, seed=33))
+    wr = (torch.randn((E, H), generator=torch.Generator().manual_seed(34)) * 0.02).cuda()
+    y = B.add_rmsnorm(x, w, 1e-6, r, bf16=False, residual_out=False)["f32"]
+    logits = B.router_logits_f32(y, wr)
+    ids, wts = B.gate_topk(logits, k, B.GATE_SOFTMAX)
+    torch.cuda.synchronize()
+    gl = logits.cpu().numpy()
+    ref = y.double().cpu().numpy() @ wr.double().cpu().numpy().T
+    np.testing.assert_allclose(gl.astype(np.float64), ref, atol=ATOL_LOGITS, rtol=0)
+    want_ids, want_w = moe.gate_topk_softmax(gl, k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), want_ids)
+    np.testing.assert_allclose(wts.cpu().numpy(), want_w, rtol=1e-6, atol=1e-7)

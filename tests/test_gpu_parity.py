@@ -270,16 +270,18 @@ def test_layer_zero_tokens():
     assert out.shape == (0, L.cfg.H)
 
 
-def test_layer_deterministic():
-    L = get_layer(SMALL["small_hy3"])
+@pytest.mark.parametrize("name", ["small_hy3", "tiled4_stream"])
+def test_layer_deterministic(name):
+    L = get_layer(SMALL[name])
     layer = L.layer()
     a = layer.forward(L.dev["x"]).clone()
     b = layer.forward(L.dev["x"]).clone()
     assert torch.equal(a, b)
 
 
-def test_layer_graph_capture_replays():
-    L = get_layer(SMALL["small_prefill"])
+@pytest.mark.parametrize("name", ["small_prefill", "tiled4_hy3"])
+def test_layer_graph_capture_replays(name):
+    L = get_layer(SMALL[name])
     layer = L.layer()
     x = L.dev["x"]
     out = torch.empty((x.shape[0], L.cfg.H), dtype=torch.bfloat16, device="cuda")
