@@ -341,10 +341,12 @@ def test_one_expert_layer_is_the_plain_mlp():
     assert_close_bf16(bf16_np(out), ref, ATOL, RTOL, "one expert")
 
 
-def test_all_tokens_on_one_expert():
+@pytest.mark.parametrize("T,H,I", [(300, 256, 128), (1000, 512, 384)])
+def test_all_tokens_on_one_expert(T, H, I):
     """A router bias that makes expert 3 win for every token: one group holds
-    all rows, the others none (ragged extreme)."""
-    cfg = CFG["tiny"].with_(name="skew", T=300, E=8, k=1, x_seed=35)
+    all rows, the others none (ragged extreme; the second shape runs the
+    one-wave-per-SIMD tiled kernels with 8 m-tiles in one group)."""
+    cfg = CFG["tiny"].with_(name=f"skew_{H}", T=T, H=H, I=I, E=8, k=1, x_seed=35, family_seed=1035 + H)
     L = get_layer(cfg)
     bias = torch.zeros(cfg.E)
     bias[3] = 1000.0
