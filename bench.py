@@ -119,7 +119,18 @@ def _counter_means(path):
     return {k: sum(v) / len(v) for k, v in d.items()}
 
 
-def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+COUNTER_TITLES = {
+    "qwen3_decode": "Qwen3-style decode layer (T=16, H=4096, E=128, top-8, I=1536, bf16)",
+    "qwen3_prefill": "Qwen3-style prefill layer (T=4096, H=4096, E=128, top-8, I=1536, bf16)",
+    "qwen3_decode_w4a8": "Qwen3-style decode layer with W4A8 experts (T=16, H=4096, E=128, top-8, I=1536, "
+                         "MXFP4 weights, MXFP8 activations, Zipf router bias)",
+    "qwen3_prefill_w4a8": "Qwen3-style prefill layer with W4A8 experts (T=4096, H=4096, E=128, top-8, I=1536, "
+                          "MXFP4 weights, MXFP8 activations)",
+    "add_rmsnorm": "residual add + RMSNorm before the layer (T=4096, H=4096, fp32 + bf16 outputs, bf16 residual)",
+}
+
+
+def summarize_counters(config, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     """Markdown summary of HBM byte counters per kernel, scaled by what the
     same counters read for a plain 1 GiB device copy."""
     fetch, write = _counter_means(fetch_csv), _counter_means(write_csv)
@@ -127,13 +138,16 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     cw = max(v for k, v in _counter_means(copy_write_csv).items() if "copyBuffer" in k)
     kib = 1024 * 1024  # the copy moves 1 GiB = 1,048,576 KiB each way
     sf, sw = kib / cf, kib / cw
-    lines = [f"# HBM byte counters, Qwen3-style decode layer (T=16, H=4096, E=128, top-8, I=1536, bf16)", "",
+    cfg_arg = "" if config == "qwen3_decode" else f" --config {config}"
+    run = f"python $R/bench.py{cfg_arg} --steps 5 --warmup 2 --no-cpu-baseline"
+    lines = [f"# HBM byte counters, {COUNTER_TITLES.get(config, config)}", "",
              "Each counter in its own pass (run from /tmp on one MI355X, repo at $R):", "", "```",
-             "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE_decode -o run --output-format csv -- python $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
-             "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_WRITE_SIZE_decode -o run --output-format csv -- python $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+             f"rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE_{config} -o run --output-format csv -- {run}",
+             f"rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_WRITE_SIZE_{config} -o run --output-format csv -- {run}",
              "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
              "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_WRITE_SIZE_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
-             "python $R/bench.py --summarize-counters <the four run_counter_collection.csv files>", "```", "",
+             f"python $R/bench.py --config {config} --summarize-counters <the four run_counter_collection.csv files>",
+             "```", "",
              f"Calibration (1 GiB device copy): FETCH_SIZE {cf:,.1f} KiB -> scale x{sf:.3f}; "
              f"WRITE_SIZE {cw:,.1f} KiB -> scale x{sw:.3f}.", "",
              "| kernel | FETCH_SIZE KiB | read bytes (scaled) | WRITE_SIZE KiB | written bytes (scaled) |",
@@ -146,11 +160,13 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
         lines.append(f"| `{k[:80]}` | {fetch[k]:,.1f} | {rb / 1e9:.4f} GB | {write.get(k, 0.0):,.1f} | {wb / 1e6:.3f} MB |")
         if GEMM1_KERNEL in k:
             g1 = (rb, wb)
-    lines += ["", "Machine-readable (bench.py reports `roofline.traffic` from these only while the GEMM1 "
-              "sources still hash to the value below):", "",
-              f"gemm1_source_sha256_16: {gemm1_source_hash()}",
-              f"gemm1_read_bytes: {int(g1[0]) if g1 else 0}",
-              f"gemm1_write_bytes: {int(g1[1]) if g1 else 0}", ""]
+    if config == "qwen3_decode":
+        lines += ["", "Machine-readable (bench.py reports `roofline.traffic` from these only while the GEMM1 "
+                  "sources still hash to the value below):", "",
+                  f"gemm1_source_sha256_16: {gemm1_source_hash()}",
+                  f"gemm1_read_bytes: {int(g1[0]) if g1 else 0}",
+                  f"gemm1_write_bytes: {int(g1[1]) if g1 else 0}"]
+    lines.append("")
     print("\n".join(lines))
 
 
@@ -317,7 +333,7 @@ def bench_norm(args):
 def main():
     args = parse()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(args.config, *args.summarize_counters)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
