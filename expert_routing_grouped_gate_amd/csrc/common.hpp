@@ -224,4 +224,62 @@ struct TileMap {
   }
 };
 
+// TileMap's per-lane state, parked in LDS between the tiles of a persistent
+// block so that it costs no registers during a K loop: kTileMapWords words per
+// lane, `slot` = this wave's [kTileMapWords][64] ints.  Parked only when the
+// map has groups (offsets != nullptr); the identity map needs nothing.
+constexpr int kTileMapWords = 13;
+
+__device__ __forceinline__ void park_tilemap(const TileMap& tm, int* slot) {
+  int* mine = slot + (threadIdx.x & 63);
+  mine[0] = tm.excl;
+  mine[64] = tm.gbeg;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) mine[64 * (2 + i)] = tm.tiles[i];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) mine[64 * (7 + i)] = tm.o[i];
+}
+
+__device__ __forceinline__ TileMap unpark_tilemap(const int* slot, const int* offsets,
+                                                  int ident_rows, int total, int BM) {
+  TileMap tl;
+  tl.offsets = offsets;
+  tl.ident_rows = ident_rows;
+  tl.total = total;
+  tl.BM = BM;
+  if (offsets != nullptr) {
+    const int* mine = slot + (threadIdx.x & 63);
+    tl.excl = mine[0];
+    tl.gbeg = mine[64];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) tl.tiles[i] = mine[64 * (2 + i)];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) tl.o[i] = mine[64 * (7 + i)];
+  }
+  return tl;
+}
+
+// One output tile of a grouped GEMM (wave-uniform).
+struct TileRef {
+  int grp, n_tile, row0, nrows;
+};
+
+// Tile `id` (after xcd_remap) of the expert-major order: group, then n-tile,
+// then the group's m-tiles.  The m-tiles that share a weight tile are
+// neighbours (they start together and the weight tile streams through L2
+// once), and a group's tiles stay on one XCD.
+__device__ __forceinline__ TileRef expert_major_tile(const TileMap& tl, int id, int n_tiles) {
+  int grp, first_mt, n_mt, grow0, grow1;
+  tl.find_group(id / n_tiles, grp, first_mt, n_mt, grow0, grow1);
+  const int local = id - first_mt * n_tiles;
+  const int n_tile = local / n_mt;
+  const int row0 = grow0 + (local - n_tile * n_mt) * tl.BM;
+  TileRef r;
+  r.grp = __builtin_amdgcn_readfirstlane(grp);
+  r.n_tile = __builtin_amdgcn_readfirstlane(n_tile);
+  r.row0 = __builtin_amdgcn_readfirstlane(row0);
+  r.nrows = __builtin_amdgcn_readfirstlane(min(tl.BM, grow1 - row0));
+  return r;
+}
+
 }  // namespace moe

@@ -347,19 +347,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void ffn_tiled(GroupedGemm g, in
   TileMap tm;
   tm.init(g.offsets, g.G, g.ident_rows, BM, g.total_rows);
   const int total = tm.total * n_tiles;
-  // Tile order: expert-major, then n-tile, then the expert's m-tiles.  The
-  // m-tiles that share a weight tile are neighbours (they start together and
-  // the weight tile streams through L2 once), and the ~n_tiles x m-tiles
-  // tiles of an expert fit in the concurrent blocks of one XCD, so its
-  // gathered activation rows stay in that L2 for all n-tiles.
+  // Tile order: expert_major_tile (the ~n_tiles x m-tiles tiles of an expert
+  // fit in the concurrent blocks of one XCD, so its gathered activation rows
+  // stay in that L2 for all n-tiles).
   for (int t = blockIdx.x; t < total; t += gridDim.x) {
-    const int id = xcd_remap(t, total);
-    int grp, first_mt, n_mt, grow0, grow1;
-    tm.find_group(id / n_tiles, grp, first_mt, n_mt, grow0, grow1);
-    const int local = id - first_mt * n_tiles;
-    const int n_tile = local / n_mt;
-    const int row0 = grow0 + (local - n_tile * n_mt) * BM;
-    tiled_tile<SWIGLU, BM, BN, WM, WN, NS>(g, smem, n_tile, grp, row0, min(BM, grow1 - row0));
+    const TileRef r = expert_major_tile(tm, xcd_remap(t, total), n_tiles);
+    tiled_tile<SWIGLU, BM, BN, WM, WN, NS>(g, smem, r.n_tile, r.grp, r.row0, r.nrows);
   }
 }
 

@@ -89,12 +89,10 @@ template <bool SWIGLU, int WM, int WN, int NS>
 __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, int n_tiles) {
   using C = MxTiled<SWIGLU, WM, WN, NS>;
   constexpr int MT = C::MT, NT = C::NT;
-  // One LDS array: the ring, then the scheduler's per-lane table (13 values
-  // per lane, one copy per wave), parked here between tiles, where it costs
-  // no registers in the K loop.  (A second __shared__ variable makes the
+  // One LDS array: the ring, then the scheduler's per-lane table (one copy
+  // per wave, park_tilemap).  (A second __shared__ variable makes the
   // compiler wait for every outstanding DMA to LDS before each LDS read.)
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE + C::NW * 13 * 64 * 4];
-  int(*tm_lds)[13][64] = reinterpret_cast<int(*)[13][64]>(smem + NS * C::STAGE);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE + C::NW * kTileMapWords * 64 * 4];
   TileMap tm;
   tm.init(g.offsets, g.G, g.ident_rows, C::BM, g.total_rows);
   const int total = __builtin_amdgcn_readfirstlane(tm.total * n_tiles);
@@ -104,15 +102,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (g.offsets != nullptr) {
-    int* mine = &tm_lds[wave][0][lane];
-    mine[0] = tm.excl;
-    mine[64] = tm.gbeg;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) mine[64 * (2 + i)] = tm.tiles[i];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) mine[64 * (7 + i)] = tm.o[i];
-  }
+  int* const tm_slot = reinterpret_cast<int*>(smem + NS * C::STAGE) + wave * kTileMapWords * 64;
+  if (g.offsets != nullptr) park_tilemap(tm, tm_slot);
   const int wm = wave % WM, wn = wave / WM;
   const int li = lane & 15, kb = lane >> 4;
   const int K = g.K, ns = K / 128, nq = ns / 4;  // nq >= 2 (launcher)
@@ -123,31 +114,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
   const uint32_t wscale_bytes = wrows / 16u * (uint32_t)nq * 256u;
 
   auto locate = [&](int tt) {
-    const int id = xcd_remap(tt, total);
-    TileMap tl;
-    tl.offsets = g.offsets;
-    tl.ident_rows = g.ident_rows;
-    tl.total = tm.total;
-    tl.BM = C::BM;
-    if (g.offsets != nullptr) {
-      const int* mine = &tm_lds[wave][0][lane];
-      tl.excl = mine[0];
-      tl.gbeg = mine[64];
-#pragma unroll
-      for (int i = 0; i < 5; ++i) tl.tiles[i] = mine[64 * (2 + i)];
-#pragma unroll
-      for (int i = 0; i < 6; ++i) tl.o[i] = mine[64 * (7 + i)];
-    }
-    int grp, first_mt, n_mt, grow0, grow1;
-    tl.find_group(id / n_tiles, grp, first_mt, n_mt, grow0, grow1);
-    const int local = id - first_mt * n_tiles;
-    const int n_tile = local / n_mt;
-    const int row0 = grow0 + (local - n_tile * n_mt) * C::BM;
+    const TileMap tl = unpark_tilemap(tm_slot, g.offsets, g.ident_rows, tm.total, C::BM);
+    const TileRef r = expert_major_tile(tl, xcd_remap(tt, total), n_tiles);
     MxTileInfo ti;
-    ti.grp = __builtin_amdgcn_readfirstlane(grp);
-    ti.n0 = __builtin_amdgcn_readfirstlane(n_tile * C::BNOUT);
-    ti.row0 = __builtin_amdgcn_readfirstlane(row0);
-    ti.nrows = __builtin_amdgcn_readfirstlane(min(C::BM, grow1 - row0));
+    ti.grp = r.grp;
+    ti.n0 = __builtin_amdgcn_readfirstlane(r.n_tile * C::BNOUT);
+    ti.row0 = r.row0;
+    ti.nrows = r.nrows;
     return ti;
   };
   // Per-lane rows of a tile, in two halves so that no load result is used

@@ -43,8 +43,7 @@ struct Tiled4 {
   static constexpr int LPA = BM / 8 / NW;  // 1 KB activation DMAs per wave per stage (4)
   static constexpr int LPB = BN / 8 / NW;  // 1 KB weight DMAs per wave per stage (8)
   static constexpr int LPW = LPA + LPB;
-  static constexpr int TMW = 13;           // parked scheduler words per lane
-  static_assert(NS * STAGE + NW * TMW * 64 * 4 <= 160 * 1024, "LDS");
+  static_assert(NS * STAGE + NW * kTileMapWords * 64 * 4 <= 160 * 1024, "LDS");
 };
 
 struct T4Tile {
@@ -67,11 +66,9 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   using C = Tiled4<SWIGLU>;
   constexpr int MT = C::MT, NT = C::NT, NW = C::NW;
   // One LDS array: the ring, then the scheduler's per-lane table (one copy
-  // per wave), parked here between tiles where it costs no registers in the
-  // K loop.  (A second __shared__ variable makes the compiler wait for every
-  // outstanding DMA before each LDS read.)
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE + NW * C::TMW * 64 * 4];
-  int(*tm_lds)[C::TMW][64] = reinterpret_cast<int(*)[C::TMW][64]>(smem + C::NS * C::STAGE);
+  // per wave, park_tilemap).  (A second __shared__ variable makes the
+  // compiler wait for every outstanding DMA before each LDS read.)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE + NW * kTileMapWords * 64 * 4];
   TileMap tm;
   tm.init(g.offsets, g.G, g.ident_rows, C::BM, g.total_rows);
   const int total = __builtin_amdgcn_readfirstlane(tm.total * n_tiles);
@@ -81,15 +78,8 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (g.offsets != nullptr) {
-    int* mine = &tm_lds[wave][0][lane];
-    mine[0] = tm.excl;
-    mine[64] = tm.gbeg;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) mine[64 * (2 + i)] = tm.tiles[i];
-#pragma unroll
-    for (int i = 0; i < 6; ++i) mine[64 * (7 + i)] = tm.o[i];
-  }
+  int* const tm_slot = reinterpret_cast<int*>(smem + C::NS * C::STAGE) + wave * kTileMapWords * 64;
+  if (g.offsets != nullptr) park_tilemap(tm, tm_slot);
   const int wm = wave % C::WM, wn = wave / C::WM;
   const int li = lane & 15, kc = lane >> 4;
   const int K = g.K, nk = K / 64;  // nk >= 5 (launcher)
@@ -101,34 +91,13 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   const uint32_t dchunk = 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
 
   auto locate = [&](int tt) {
-    const int id = xcd_remap(tt, total);
-    TileMap tl;
-    tl.offsets = g.offsets;
-    tl.ident_rows = g.ident_rows;
-    tl.total = tm.total;
-    tl.BM = C::BM;
-    if (g.offsets != nullptr) {
-      const int* mine = &tm_lds[wave][0][lane];
-      tl.excl = mine[0];
-      tl.gbeg = mine[64];
-#pragma unroll
-      for (int i = 0; i < 5; ++i) tl.tiles[i] = mine[64 * (2 + i)];
-#pragma unroll
-      for (int i = 0; i < 6; ++i) tl.o[i] = mine[64 * (7 + i)];
-    }
-    // expert-major, then n-tile, then the expert's m-tiles: the m-tiles that
-    // share a weight tile are neighbours, and an expert's tiles stay on one
-    // XCD (xcd_remap)
-    int grp, first_mt, n_mt, grow0, grow1;
-    tl.find_group(id / n_tiles, grp, first_mt, n_mt, grow0, grow1);
-    const int local = id - first_mt * n_tiles;
-    const int n_tile = local / n_mt;
-    const int row0 = grow0 + (local - n_tile * n_mt) * C::BM;
+    const TileMap tl = unpark_tilemap(tm_slot, g.offsets, g.ident_rows, tm.total, C::BM);
+    const TileRef r = expert_major_tile(tl, xcd_remap(tt, total), n_tiles);
     T4Tile ti;
-    ti.grp = __builtin_amdgcn_readfirstlane(grp);
-    ti.n0 = __builtin_amdgcn_readfirstlane(n_tile * C::BNOUT);
-    ti.row0 = __builtin_amdgcn_readfirstlane(row0);
-    ti.nrows = __builtin_amdgcn_readfirstlane(min(C::BM, grow1 - row0));
+    ti.grp = r.grp;
+    ti.n0 = __builtin_amdgcn_readfirstlane(r.n_tile * C::BNOUT);
+    ti.row0 = r.row0;
+    ti.nrows = r.nrows;
     return ti;
   };
   // Activation rows of this lane's LPA DMAs (group ra = wave + NW i, 8 rows;

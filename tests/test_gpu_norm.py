@@ -37,8 +37,9 @@ def _bf16_step(v):
 
 
 # (T, H): one 32-block; 12 chunks; the decode and prefill hidden size; a
-# width that leaves some threads with one chunk fewer; the largest width
-CASES = [(1, 32), (7, 96), (16, 4096), (333, 4096), (5, 2080), (64, 16384)]
+# width that leaves some threads with one chunk fewer; the largest width; the
+# prefill layer's input as the bench times it
+CASES = [(1, 32), (7, 96), (16, 4096), (333, 4096), (5, 2080), (64, 16384), (4096, 4096)]
 
 
 @pytest.mark.parametrize("with_residual", [True, False])
