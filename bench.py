@@ -268,6 +268,65 @@ NORM_CONFIGS = {
 }
 
 
+def bench_combine_norm(args):
+    """The layer's combine fused with the next step's residual add + RMSNorm
+    (moe_combine_add_rmsnorm) at the prefill layer's shape: one step = one
+    call over T tokens with the fp32 + bf16 + residual outputs; fence-free
+    HIP events around each call; the separate moe_combine + moe_add_rmsnorm
+    calls are timed the same way in the same run for comparison."""
+    import torch
+
+    from expert_routing_grouped_gate_amd import binding as B
+    from expert_routing_grouped_gate_amd import workloads as W
+
+    T, k, H = 4096, 8, 4096
+    eps = 1e-6
+    y, pp, w = (t.cuda() for t in W.draw_combine_inputs(T, k, H, seed=4097))
+    _, r, g = (t.cuda() for t in W.draw_norm_inputs(T, H, seed=4098))
+    stream = torch.cuda.current_stream().cuda_stream
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def fused():
+        B.combine_add_rmsnorm(y, pp, w, None, g, eps, r)
+
+    def separate():
+        B.combine(y, pp, w, None, out)
+        B.add_rmsnorm(out, g, eps, r)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, sum(a.elapsed_ms(b) for a, b in ev) / args.steps
+
+    ms, k_ms = timed(fused)
+    sep_ms, sep_k_ms = timed(separate)
+    alg = int(T * k * H * 2 + T * H * 2 + T * k * 8 + H * 2 + T * H * (4 + 2 + 2))
+    gbs = alg / (k_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"combine_add_rmsnorm: the layer's combine (T={T}, top-{k}, H={H}) fused with "
+                               "the next residual add + RMSNorm (fp32 + bf16 outputs, bf16 residual)",
+                   "T": T, "k": k, "H": H, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "combine_add_rmsnorm_kernel", "kernel_ms": round(k_ms, 5), "algorithmic_bytes": alg},
+        "separate": {"ms_per_step": round(sep_ms, 5), "events_ms": round(sep_k_ms, 5),
+                     "calls": "moe_combine + moe_add_rmsnorm"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def bench_norm(args):
     """The residual add + RMSNorm step (moe_add_rmsnorm) alone: one step =
     one call over T tokens, inputs resident in HBM; fence-free HIP events on
@@ -352,6 +411,9 @@ def main():
     B.load()
     if args.config in NORM_CONFIGS:
         bench_norm(args)
+        return
+    if args.config == "combine_add_rmsnorm":
+        bench_combine_norm(args)
         return
     cfg = W.CONFIGS[args.config]
     log(f"[bench] drawing {cfg.name}")

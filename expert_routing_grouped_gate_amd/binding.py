@@ -67,6 +67,8 @@ SIGNATURES = {
     "moe_route": (_I, [_vp, _I, _I, _I, _vp, _vp, _vp, _vp, _vp, _vp, _SZ, _vp]),
     "moe_mx_quantize": (_I, [_vp, _I, _I, _vp, _vp, _vp]),
     "moe_add_rmsnorm": (_I, [_vp, _vp, _vp, _I, _I, _F, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_combine_add_rmsnorm": (_I, [_vp, _vp, _vp, _vp, _I, _I, _I, _vp, _vp, _F, _vp, _vp, _vp, _vp,
+                                     _vp, _vp, _vp]),
     "moe_router_f32_workspace_size": (_SZ, [_I, _I, _I]),
     "moe_router_logits_f32": (_I, [_vp, _vp, _I, _I, _I, _vp, _vp, _SZ, _vp]),
     "moe_mx_packed_scales_bytes": (_SZ, [_I, _I]),
@@ -190,6 +192,37 @@ def mx_quantize(x: torch.Tensor):
     scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
     _check("moe_mx_quantize", load().moe_mx_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream()))
     return codes, scales
+
+
+def combine_add_rmsnorm(y, pair_pos, topk_w, shared_y, weight: torch.Tensor, eps: float,
+                        residual: Optional[torch.Tensor] = None, out: bool = False, f32: bool = True,
+                        bf16: bool = True, residual_out: bool = True, mx: bool = False):
+    """moe_combine_add_rmsnorm: the combine of the layer's expert rows, then
+    residual add + RMSNorm of the combined rows.  Returns a dict with the
+    requested outputs: "out" [T, H] bf16 (the combined rows), and "f32",
+    "bf16", "residual", "mx" as add_rmsnorm."""
+    T, k = topk_w.shape
+    H = y.shape[1]
+    _dev(y, pair_pos, topk_w, shared_y, weight, residual)
+    dev = y.device
+    res = {}
+    if out:
+        res["out"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if f32:
+        res["f32"] = torch.empty((T, H), dtype=torch.float32, device=dev)
+    if bf16:
+        res["bf16"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if residual_out:
+        res["residual"] = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    if mx:
+        res["mx"] = (torch.empty((T, H), dtype=torch.uint8, device=dev),
+                     torch.empty((T, H // 32), dtype=torch.uint8, device=dev))
+    q, qs = res.get("mx", (None, None))
+    _check("moe_combine_add_rmsnorm", load().moe_combine_add_rmsnorm(
+        _ptr(y), _ptr(pair_pos), _ptr(topk_w), _ptr(shared_y), T, k, H, _ptr(residual), _ptr(weight),
+        float(eps), _ptr(res.get("out")), _ptr(res.get("f32")), _ptr(res.get("bf16")),
+        _ptr(res.get("residual")), _ptr(q), _ptr(qs), _stream()))
+    return res
 
 
 def router_logits_f32(x: torch.Tensor, wr: torch.Tensor, out: Optional[torch.Tensor] = None):

@@ -380,6 +380,27 @@ int moe_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t*
                                  y_mx_scales, as_stream(stream));
 }
 
+int moe_combine_add_rmsnorm(const uint16_t* y, const int32_t* pair_pos, const float* topk_w,
+                            const uint16_t* shared_y, int T, int k, int H,
+                            const uint16_t* residual, const uint16_t* weight, float eps,
+                            uint16_t* out, float* y_f32, uint16_t* y_bf16, uint16_t* residual_out,
+                            uint8_t* y_mx, uint8_t* y_mx_scales, void* stream) {
+  int st;
+  if (H <= 0 || k <= 0) return MOE_ERR_SHAPE;
+  if (H % 256 != 0 || H > 16384 || k > 32) return MOE_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || eps == __builtin_inff()) return MOE_ERR_SHAPE;  // also rejects NaN
+  if ((st = check_rows(T, k))) return st;
+  if (T == 0) return MOE_OK;
+  if ((y_mx == nullptr) != (y_mx_scales == nullptr)) return MOE_ERR_NULL;
+  if (!out && !y_f32 && !y_bf16 && !residual_out && !y_mx) return MOE_ERR_NULL;
+  if ((st = check_ptrs({y, pair_pos, topk_w, weight}))) return st;
+  if ((st = check_optional({shared_y, residual, out, y_f32, y_bf16, residual_out, y_mx, y_mx_scales})))
+    return st;
+  return moe::launch_combine_add_rmsnorm(y, pair_pos, topk_w, shared_y, T, k, residual, weight, H,
+                                         eps, out, y_f32, y_bf16, residual_out, y_mx, y_mx_scales,
+                                         as_stream(stream));
+}
+
 int moe_combine(const uint16_t* y, const int32_t* pair_pos, const float* topk_w,
                 const uint16_t* shared_y, int T, int k, int H, uint16_t* out, void* stream) {
   int st;

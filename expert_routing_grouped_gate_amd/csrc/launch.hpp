@@ -94,6 +94,15 @@ int launch_add_rmsnorm(const uint16_t* x, const uint16_t* res, const uint16_t* w
                        float eps, float* yf, uint16_t* yb, uint16_t* rout, uint8_t* q,
                        uint8_t* qs, hipStream_t s);
 
+// combine (S7) of the layer's expert rows + residual add + RMSNorm of the
+// combined rows (T >= 1, 1 <= k <= 32, H % 256 == 0, H <= 16384); out (the
+// combined rows) and the norm outputs may each be null.
+int launch_combine_add_rmsnorm(const uint16_t* y, const int32_t* pair_pos, const float* tw,
+                               const uint16_t* shared_y, int T, int k, const uint16_t* res,
+                               const uint16_t* w, int H, float eps, uint16_t* out, float* yf,
+                               uint16_t* yb, uint16_t* rout, uint8_t* q, uint8_t* qs,
+                               hipStream_t s);
+
 int launch_combine(const uint16_t* y, const int32_t* pair_pos, const float* w,
                    const uint16_t* shared_y, int T, int k, int H, uint16_t* out, hipStream_t s);
 

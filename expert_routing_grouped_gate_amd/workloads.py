@@ -38,6 +38,7 @@ import torch
 _TAG_X, _TAG_ROUTER, _TAG_BIAS, _TAG_W13, _TAG_W2, _TAG_SHARED = 1, 2, 3, 4, 5, 6
 _TAG_MX_W13, _TAG_MX_W2, _TAG_MX_SHARED = 7, 8, 9
 _TAG_NORM_X, _TAG_NORM_RES, _TAG_NORM_W = 10, 11, 12
+_TAG_CMB_Y, _TAG_CMB_PERM, _TAG_CMB_W = 13, 14, 15
 
 
 @dataclass(frozen=True)
@@ -249,3 +250,15 @@ def draw_norm_inputs(T: int, H: int, seed: int):
     r = _normal((T, H), 1.0, seed, _TAG_NORM_RES, T, H).to(torch.bfloat16)
     w = (1.0 + _normal((H,), 0.1, seed, _TAG_NORM_W, H)).to(torch.bfloat16)
     return x, r, w
+
+
+def draw_combine_inputs(T: int, k: int, H: int, seed: int):
+    """Stand-ins for a layer's expert outputs at the combine: rows y
+    [T*k, H] bf16 ~ N(0, 0.05) (the size of expert outputs at these
+    shapes), pair positions [T*k] int32 = a random permutation of the rows,
+    and top-k weights [T, k] fp32 ~ U(0, 2/k)."""
+    R = T * k
+    y = _normal((R, H), 0.05, seed, _TAG_CMB_Y, R, H).to(torch.bfloat16)
+    pos = torch.randperm(R, generator=_gen(seed, _TAG_CMB_PERM, R)).to(torch.int32)
+    w = torch.rand((T, k), generator=_gen(seed, _TAG_CMB_W, T, k)) * (2.0 / k)
+    return y, pos, w

@@ -176,6 +176,25 @@ int moe_add_rmsnorm(const uint16_t* x, const uint16_t* residual, const uint16_t*
                     int H, float eps, float* y_f32, uint16_t* y_bf16, uint16_t* residual_out,
                     uint8_t* y_mx, uint8_t* y_mx_scales, void* stream);
 
+/* S7 fused with the next step's residual add + RMSNorm: the layer's output
+ * feeds the next norm without a round trip through memory ([Qwen3]
+ * "fused-operator optimisation": fusing to avoid writing and re-reading
+ * intermediate results).  Per token row: out = moe_combine's row (fp32 slot
+ * order, + shared row, rounded to bf16), then moe_add_rmsnorm of out with
+ * `residual`.  Every output equals moe_combine followed by moe_add_rmsnorm
+ * bit for bit.
+ *   y, pair_pos, topk_w, shared_y, T, k, H   as moe_combine
+ *   residual, weight, eps                    as moe_add_rmsnorm (x = out)
+ *   out          [T, H] bf16 layer output, or NULL (not stored)
+ *   y_f32, y_bf16, residual_out, y_mx, y_mx_scales   as moe_add_rmsnorm
+ * At least one output must be given.  No output may overlap an input.
+ * Limits: H % 256 == 0, H <= 16384, 1 <= k <= 32.  T == 0 enqueues nothing. */
+int moe_combine_add_rmsnorm(const uint16_t* y, const int32_t* pair_pos, const float* topk_w,
+                            const uint16_t* shared_y, int T, int k, int H,
+                            const uint16_t* residual, const uint16_t* weight, float eps,
+                            uint16_t* out, float* y_f32, uint16_t* y_bf16, uint16_t* residual_out,
+                            uint8_t* y_mx, uint8_t* y_mx_scales, void* stream);
+
 /* ------------------------------------------------------------- S0 -----
  * Dynamic MXFP8 quantisation ([Qwen3] "MoE EP optimisation": hidden_states
  * -> MXFP8 data + scale; round_mode rint, dst_type float8_e4m3fn).  Per

@@ -123,6 +123,27 @@ def test_combine_checks(lib):
     assert f(FAKE, FAKE, FAKE, None, 4, 33, 256, FAKE, None) == UNSUP
 
 
+def test_combine_add_rmsnorm_checks(lib):
+    f = lib.moe_combine_add_rmsnorm
+    args = lambda **kw: [kw.get(k, v) for k, v in (  # noqa: E731
+        ("y", FAKE), ("pp", FAKE), ("w", FAKE), ("sh", None), ("T", 4), ("k", 2), ("H", 256),
+        ("r", FAKE), ("g", FAKE), ("eps", 1e-6), ("out", None), ("yf", FAKE), ("yb", None),
+        ("ro", None), ("q", None), ("qs", None), ("s", None))]
+    assert f(*args(H=288)) == UNSUP                     # H % 256
+    assert f(*args(H=16384 + 256)) == UNSUP
+    assert f(*args(k=33)) == UNSUP
+    assert f(*args(k=0)) == SHAPE
+    assert f(*args(T=-1)) == SHAPE
+    assert f(*args(eps=float("nan"))) == SHAPE
+    assert f(*args(yf=None)) == NULL                    # no output at all
+    assert f(*args(q=FAKE)) == NULL
+    assert f(*args(pp=None)) == NULL
+    assert f(*args(g=None)) == NULL
+    assert f(*args(sh=MIS)) == ALIGN
+    assert f(*args(out=MIS)) == ALIGN
+    assert f(*args(T=0)) == OK
+
+
 def test_router_logits_f32_checks(lib):
     f = lib.moe_router_logits_f32
     ws = lib.moe_router_f32_workspace_size(4, 512, 8)

@@ -1,5 +1,8 @@
 """GPU parity of the residual add + RMSNorm before the layer
-(moe_add_rmsnorm) against the oracle (oracle/norm.py), through the C ABI.
+(moe_add_rmsnorm), the fp32-input router that consumes its output, and the
+combine fused with the norm (moe_combine_add_rmsnorm), against the oracle
+(oracle/norm.py, oracle/moe.py) and against the separate calls, through the C
+ABI.
 
 Bars: the residual output z rounded to bf16 is bit-exact (the fp32 sum of
 two bf16 values is exact); the fp32 output within 1e-5 relative (the
@@ -176,3 +179,59 @@ def test_norm_feeds_the_gate_in_fp32():
     want_ids, want_w = moe.gate_topk_softmax(gl, k)
     np.testing.assert_array_equal(ids.cpu().numpy(), want_ids)
     np.testing.assert_allclose(wts.cpu().numpy(), want_w, rtol=1e-6, atol=1e-7)
+
+
+# ------------------------- S7 fused with the next layer's add + RMSNorm ----
+
+def _separate(y, pp, w, shared, weight, eps, res):
+    out = B.combine(y, pp, w, shared)
+    n = B.add_rmsnorm(out, weight, eps, res, mx=True)
+    return out, n
+
+
+@pytest.mark.parametrize("with_shared,with_residual", [(True, True), (False, True), (False, False)])
+def test_combine_add_rmsnorm_equals_separate_calls_on_a_layer(with_shared, with_residual):
+    """The expert rows of a real layer (the one-wave-per-SIMD tiled path,
+    sigmoid gating, shared expert): every output of the fused call equals
+    moe_combine then moe_add_rmsnorm bit for bit; the combined rows match the
+    oracle's combine of the same expert rows."""
+    from oracle import moe
+    from tests.layer_fixtures import get_layer
+    cfg = W.CONFIGS["hy3"].with_(name="fuse_hy3", T=300, H=512, E=16, k=4, I=384, shared_I=384,
+                                 x_seed=41, family_seed=1041)
+    L = get_layer(cfg)
+    layer = L.layer()
+    layer.forward(L.dev["x"])
+    b = layer.buf
+    shared = b["shared_y"] if with_shared else None
+    g = torch.Generator().manual_seed(42)
+    res = torch.randn((cfg.T, cfg.H), generator=g).to(torch.bfloat16).cuda() if with_residual else None
+    weight = (1 + 0.1 * torch.randn(cfg.H, generator=g)).to(torch.bfloat16).cuda()
+    fused = B.combine_add_rmsnorm(b["y"], b["pair_pos"], b["topk_w"], shared, weight, 1e-6, res,
+                                  out=True, mx=True)
+    out, n = _separate(b["y"], b["pair_pos"], b["topk_w"], shared, weight, 1e-6, res)
+    torch.cuda.synchronize()
+    assert torch.equal(fused["out"], out)
+    for key in ("f32", "bf16", "residual"):
+        assert torch.equal(fused[key], n[key]), key
+    assert torch.equal(fused["mx"][0], n["mx"][0]) and torch.equal(fused["mx"][1], n["mx"][1])
+    ref = moe.combine(b["y"].double().cpu().numpy(), b["pair_pos"].cpu().numpy(),
+                      b["topk_w"].cpu().numpy(), None if shared is None else shared.double().cpu().numpy())
+    got = out.double().cpu().numpy()
+    assert np.all(np.abs(got - ref) <= _bf16_step(ref) + 1e-30)   # fp32 vs fp64 sums: one bf16 step
+
+
+@pytest.mark.parametrize("T,k,H", [(4096, 8, 4096), (16, 8, 4096), (3, 32, 256), (7, 1, 16384)])
+def test_combine_add_rmsnorm_equals_separate_calls(T, k, H):
+    """Synthetic expert rows at the prefill layer's full size and at the
+    limits (k = 32, the widest H): the fused call equals the separate ones."""
+    y, pp, w = W.draw_combine_inputs(T, k, H, seed=T + k + H)
+    x, r, g = W.draw_norm_inputs(T, H, seed=7 * T + H)
+    y, pp, w, r, g = y.cuda(), pp.cuda(), w.cuda(), r.cuda(), g.cuda()
+    fused = B.combine_add_rmsnorm(y, pp, w, None, g, 1e-6, r, out=True, mx=True)
+    out, n = _separate(y, pp, w, None, g, 1e-6, r)
+    torch.cuda.synchronize()
+    assert torch.equal(fused["out"], out)
+    for key in ("f32", "bf16", "residual"):
+        assert torch.equal(fused[key], n[key]), key
+    assert torch.equal(fused["mx"][0], n["mx"][0]) and torch.equal(fused["mx"][1], n["mx"][1])
