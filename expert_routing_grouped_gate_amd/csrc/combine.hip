@@ -3,7 +3,7 @@
 // weights) plus the always-on shared expert's row ([Hy3] section 1.1).
 //
 // Grid (T, H / 2048): a block covers 2048 hidden elements of one token, each
-// thread 8 consecutive ones (16-byte loads/stores, combine_chunk8: the rows
+// thread 8 consecutive ones (16-byte loads/stores, combine_chunks: the rows
 // of up to 8 slots loaded together, then accumulated in slot order in fp32,
 // so the result does not depend on scheduling).
 #include "common.hpp"
@@ -23,9 +23,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   const int R = (int)gridDim.x * k;
   const int c = blockIdx.y * CB_COLS + threadIdx.x * 8;
   if (c >= H) return;  // no barriers below
-  const u32x4 o = combine_chunk8(y, pair_pos + (size_t)t * k, w + (size_t)t * k,
-                                 shared_y ? shared_y + (size_t)t * H : nullptr, k, R, H, c);
-  *reinterpret_cast<u32x4*>(out + (size_t)t * H + c) = o;
+  u32x4 o[1];
+  combine_chunks<1>(y, pair_pos + (size_t)t * k, w + (size_t)t * k,
+                    shared_y ? shared_y + (size_t)t * H : nullptr, k, R, H, c, o);
+  *reinterpret_cast<u32x4*>(out + (size_t)t * H + c) = o[0];
 }
 
 int launch_combine(const uint16_t* y, const int32_t* pair_pos, const float* w,

@@ -12,7 +12,7 @@
 // One block of 256 threads per row (norm_row in rowops.hpp): the row's
 // chunks stay in registers, so x and r are read once and every output is
 // written once.  The fused form takes x from the combine of the layer's
-// expert rows (combine_chunk8), the layer output the next layer's norm reads:
+// expert rows (combine_chunks), the layer output the next layer's norm reads:
 // the combined row is rounded to bf16 exactly as moe_combine stores it, so the
 // fusion reproduces moe_combine followed by moe_add_rmsnorm bit for bit while
 // the combined row never round-trips through memory (it is stored only if
@@ -28,7 +28,7 @@ __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ res,
     const uint16_t* __restrict__ w, int H, float eps, NormOut o) {
   const size_t off = (size_t)blockIdx.x * H;
-  norm_row<NCH>([&](int c) { return ld16(x + off + c); }, res, w, H, eps, blockIdx.x, o);
+  norm_row<NCH>([&](int, int c) { return ld16(x + off + c); }, res, w, H, eps, blockIdx.x, o);
 }
 
 template <int NCH>
@@ -42,13 +42,16 @@ __global__ __launch_bounds__(kNormThreads) void combine_add_rmsnorm_kernel(
   const int32_t* pp = pair_pos + (size_t)t * k;
   const float* wt = tw + (size_t)t * k;
   const uint16_t* srow = shared_y ? shared_y + (size_t)t * H : nullptr;
-  norm_row<NCH>(
-      [&](int c) {
-        const u32x4 v = combine_chunk8(y, pp, wt, srow, k, R, H, c);
-        if (out) *reinterpret_cast<u32x4*>(out + (size_t)t * H + c) = v;
-        return v;
-      },
-      res, w, H, eps, t, o);
+  // every chunk of this thread combined first (all slot rows in flight at once)
+  u32x4 xv[NCH];
+  const int c0 = 8 * (int)threadIdx.x;
+  combine_chunks<NCH>(y, pp, wt, srow, k, R, H, c0, xv);
+  if (out) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+      if (c0 + 2048 * j < H) *reinterpret_cast<u32x4*>(out + (size_t)t * H + c0 + 2048 * j) = xv[j];
+  }
+  norm_row<NCH>([&](int j, int) { return xv[j]; }, res, w, H, eps, t, o);
 }
 
 template <int NCH>

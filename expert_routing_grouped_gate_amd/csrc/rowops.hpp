@@ -9,52 +9,68 @@
 
 namespace moe {
 
-// finalize_routing for 8 consecutive hidden elements c .. c+7 of token t
-// ([Qwen3] "GMM enablement and routing optimisation": expert outputs back in
-// token order, summed with the top-k weights; [Hy3] section 1.1: plus the
-// shared expert's row): fp32 accumulation in slot order (rows of up to 8
-// slots loaded together), the shared row added last, rounded to bf16.
-// pos >= R (outside the rows of y) or < 0 counts as a dropped pair.
-__device__ __forceinline__ u32x4 combine_chunk8(const uint16_t* __restrict__ y,
-                                                const int32_t* __restrict__ pp,
-                                                const float* __restrict__ wt,
-                                                const uint16_t* __restrict__ shared_row, int k,
-                                                int R, int H, int c) {
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+// finalize_routing for NCH chunks of 8 consecutive hidden elements of one
+// token (chunk j at element c0 + 2048 j; chunks at or past H are skipped and
+// return zero) ([Qwen3] "GMM enablement and routing optimisation": expert
+// outputs back in token order, summed with the top-k weights; [Hy3] section
+// 1.1: plus the shared expert's row): per element, fp32 accumulation in slot
+// order, the shared row added last, rounded to bf16.  The rows of up to 8
+// slots are loaded for every chunk before any of them is accumulated, so a
+// thread has all its loads in flight at once.  pos >= R (outside the rows of
+// y) or < 0 counts as a dropped pair.
+template <int NCH>
+__device__ __forceinline__ void combine_chunks(const uint16_t* __restrict__ y,
+                                               const int32_t* __restrict__ pp,
+                                               const float* __restrict__ wt,
+                                               const uint16_t* __restrict__ shared_row, int k,
+                                               int R, int H, int c0, u32x4 (&res)[NCH]) {
+  float acc[NCH][8];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
   for (int j0 = 0; j0 < k; j0 += 8) {
     int pos[8];
-    u32x4 v[8];
+    u32x4 v[NCH][8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       pos[u] = j0 + u < k ? pp[j0 + u] : -1;
       if (pos[u] >= R) pos[u] = -1;
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = pos[u] >= 0 ? ld16(y + (size_t)pos[u] * H + c) : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < NCH; ++j) {
+      const int c = c0 + 2048 * j;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[j][u] = (pos[u] >= 0 && c < H) ? ld16(y + (size_t)pos[u] * H + c) : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (pos[u] < 0) continue;
       const float wj = wt[j0 + u];
 #pragma unroll
+      for (int j = 0; j < NCH; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[j][2 * q] = fmaf(wj, bf16_to_f32(v[j][u][q] & 0xffffu), acc[j][2 * q]);
+          acc[j][2 * q + 1] = fmaf(wj, bf16_to_f32(v[j][u][q] >> 16), acc[j][2 * q + 1]);
+        }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = c0 + 2048 * j;
+    if (shared_row != nullptr && c < H) {
+      const u32x4 v = ld16(shared_row + c);
+#pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = fmaf(wj, bf16_to_f32(v[u][q] & 0xffffu), acc[2 * q]);
-        acc[2 * q + 1] = fmaf(wj, bf16_to_f32(v[u][q] >> 16), acc[2 * q + 1]);
+        acc[j][2 * q] += bf16_to_f32(v[q] & 0xffffu);
+        acc[j][2 * q + 1] += bf16_to_f32(v[q] >> 16);
       }
     }
-  }
-  if (shared_row != nullptr) {
-    const u32x4 v = ld16(shared_row + c);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[2 * q] += bf16_to_f32(v[q] & 0xffffu);
-      acc[2 * q + 1] += bf16_to_f32(v[q] >> 16);
-    }
+    for (int q = 0; q < 4; ++q) res[j][q] = pack_bf16x2(acc[j][2 * q], acc[j][2 * q + 1]);
   }
-  u32x4 o;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-  return o;
 }
 
 // Outputs of the residual add + RMSNorm of one row (each may be null; q and
@@ -72,10 +88,10 @@ constexpr int kNormThreads = 256;
 // Residual add + RMSNorm of row `row` by a block of kNormThreads threads
 // ([Notes] section 2, "Add and RMSNorm": z = x + r, y_i = z_i /
 // sqrt(mean_j z_j^2 + eps) * w_i).  Thread t holds the 16-byte chunks
-// c = t + 256 j (8 elements each) in registers: xchunk(c) returns the bf16
-// x of chunk c; z = x + r in fp32 (exact for bf16 inputs); the sum of squares
-// in fp32 in a fixed order (chunk order per thread, a butterfly over the
-// wave, then the four waves); 1/sqrt(mean + eps) in fp64 once per row;
+// c = t + 256 j (8 elements each, element offset 8 c = 8 t + 2048 j) in
+// registers: xchunk(j, 8 c) returns the bf16 x of its chunk j; z = x + r in
+// fp32 (exact for bf16 inputs); the sum of squares in fp32 in a fixed order
+// (chunk order per thread, a butterfly over the wave, then the four waves); 1/sqrt(mean + eps) in fp64 once per row;
 // y = z * rstd * w in fp32; the MXFP8 output quantises that y per 32-element
 // block (four consecutive threads) with the rule of moe_mx_quantize.
 // H % 32 == 0; NCH >= ceil(H / 8 / 256).  Contains one block barrier: every
@@ -93,7 +109,7 @@ __device__ __forceinline__ void norm_row(XChunk xchunk, const uint16_t* __restri
   for (int j = 0; j < NCH; ++j) {
     const int c = tid + kNormThreads * j;
     if (c < nch) {
-      const u32x4 xv = xchunk(8 * c);
+      const u32x4 xv = xchunk(j, 8 * c);
       const u32x4 rv = res ? ld16(res + off + 8 * c) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
