@@ -272,31 +272,43 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
 
     // ---- epilogue (registers -> global) -----------------------------------
     // D[n][m]: lane (li, kc) holds activation row li of group mi and, for
-    // weight group ni, weight rows (= output columns) 4 kc .. 4 kc + 3.
+    // weight group ni, weight rows (= output columns) 4 kc .. 4 kc + 3.  For a
+    // pair of groups (ni, ni + 1) the lanes of 16-lane rows kc and kc ^ 1 swap
+    // halves (v_permlane16_swap), so that an even-kc lane holds 8 consecutive
+    // columns of group ni and its odd partner 8 of group ni + 1: one 16-byte
+    // store per lane and pair instead of two 8-byte ones.
     uint16_t* out = static_cast<uint16_t*>(g.out);
+    constexpr int NG = SWIGLU ? NT / 2 : NT;  // output groups per wave
+    const int odd = kc & 1;
+    const int col = (SWIGLU ? 64 : 128) * wn + 8 * (kc >> 1);
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
       const int r = 64 * wm + 16 * mi + li;
-      if (r < cur.nrows) {
-        uint16_t* orow = out + (size_t)(cur.row0 + r) * g.N + cur.n0 + 4 * kc;
-        if (SWIGLU) {
+      uint16_t* orow = out + (size_t)(cur.row0 + min(r, cur.nrows - 1)) * g.N + cur.n0 + col;
 #pragma unroll
-          for (int ni = 0; ni < NT / 2; ++ni) {
-            const f32x4 gt = acc[mi][ni], up = acc[mi][ni + NT / 2];
-            u32x2 pk;
-            pk.x = pack_bf16x2(silu_fast(gt[0]) * up[0], silu_fast(gt[1]) * up[1]);
-            pk.y = pack_bf16x2(silu_fast(gt[2]) * up[2], silu_fast(gt[3]) * up[3]);
-            *reinterpret_cast<u32x2*>(orow + 64 * wn + 16 * ni) = pk;
-          }
-        } else {
+      for (int np = 0; np < NG; np += 2) {
+        u32x2 pk[2];
 #pragma unroll
-          for (int ni = 0; ni < NT; ++ni) {
-            u32x2 pk;
-            pk.x = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
-            pk.y = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
-            *reinterpret_cast<u32x2*>(orow + 128 * wn + 16 * ni) = pk;
-          }
+        for (int h = 0; h < 2; ++h) {
+          const int ni = np + h;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] = SWIGLU ? silu_fast(acc[mi][ni][i]) * acc[mi][ni + NT / 2][i] : acc[mi][ni][i];
+          pk[h].x = pack_bf16x2(v[0], v[1]);
+          pk[h].y = pack_bf16x2(v[2], v[3]);
         }
+        // vdst = group np, vsrc = group np + 1: odd rows receive the even
+        // partner's np + 1 words, even rows the odd partner's np words
+        const auto s0 = __builtin_amdgcn_permlane16_swap(pk[0].x, pk[1].x, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(pk[0].y, pk[1].y, false, false);
+        u32x4 o;
+        if (odd) {
+          o = u32x4{s0[0], s1[0], pk[1].x, pk[1].y};  // group np + 1, columns 8 (kc>>1) ..
+        } else {
+          o = u32x4{pk[0].x, pk[0].y, s0[1], s1[1]};  // group np, columns 8 (kc>>1) ..
+        }
+        if (r < cur.nrows) *reinterpret_cast<u32x4*>(orow + 16 * (np + odd)) = o;
       }
     }
     if (!has_next) {
