@@ -410,15 +410,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
               g.out_scales[(size_t)(cur.row0 + r) * (g.N / 32) + col0 / 32] = (uint8_t)(e + 127);
           }
         }
-      } else if (r < cur.nrows) {
-        uint16_t* orow = static_cast<uint16_t*>(g.out) + (size_t)(cur.row0 + r) * g.N + cur.n0 +
-                         16 * wn * NT + 4 * kb;
+      } else {
+        // groups (ni, ni + 1): lanes of 16-lane rows kb and kb ^ 1 swap halves
+        // (v_permlane16_swap) so that each lane stores 8 consecutive columns
+        // (even kb: group ni, odd kb: group ni + 1) with one 16-byte store
+        const int odd = kb & 1;
+        uint16_t* orow = static_cast<uint16_t*>(g.out) +
+                         (size_t)(cur.row0 + min(r, cur.nrows - 1)) * g.N + cur.n0 + 16 * wn * NT +
+                         8 * (kb >> 1);
 #pragma unroll
-        for (int ni = 0; ni < NT; ++ni) {
-          u32x2 pk;
-          pk.x = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
-          pk.y = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
-          *reinterpret_cast<u32x2*>(orow + 16 * ni) = pk;
+        for (int ni = 0; ni < NT; ni += 2) {
+          const uint32_t a0 = pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]);
+          const uint32_t a1 = pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3]);
+          const uint32_t b0 = pack_bf16x2(acc[mi][ni + 1][0], acc[mi][ni + 1][1]);
+          const uint32_t b1 = pack_bf16x2(acc[mi][ni + 1][2], acc[mi][ni + 1][3]);
+          const auto s0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+          const u32x4 o = odd ? u32x4{s0[0], s1[0], b0, b1} : u32x4{a0, a1, s0[1], s1[1]};
+          if (r < cur.nrows) *reinterpret_cast<u32x4*>(orow + 16 * (ni + odd)) = o;
         }
       }
     }
