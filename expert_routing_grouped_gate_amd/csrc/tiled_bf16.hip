@@ -117,6 +117,9 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
       for (int i = 0; i < C::LPA; ++i) raw[i] = g.sorted_pair[r[i]];
     }
   };
+  // Rows past the tile end get an offset past the end of A: the buffer load
+  // returns zeros without touching memory (those rows are never stored).
+  const uint32_t a_oob = (uint32_t)arows_total * rowb;
   auto gather_finish = [&](const T4Tile& ti, const int* raw, uint32_t* adma) {
     int r[C::LPA];
     tile_rows(ti, r);
@@ -124,7 +127,8 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
     for (int i = 0; i < C::LPA; ++i) {
       const uint32_t arow = GATHER ? (uint32_t)min(max(raw[i], 0) / g.topk, arows_total - 1)
                                    : (uint32_t)r[i];
-      adma[i] = arow * rowb + dchunk;
+      const bool pad = 8 * (wave + NW * i) + (lane >> 3) >= ti.nrows;
+      adma[i] = pad ? a_oob : arow * rowb + dchunk;
     }
   };
   // Weight rows of this lane's LPB DMAs relative to the tile's n0 (group rb =
