@@ -147,15 +147,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
       for (int j = 0; j < NRAW; ++j) raw[j] = r[j];
     }
   };
-  auto gather_finish = [&](const int* raw, uint32_t* adma, uint32_t* aoff) {
+  // (DMA rows past the tile end get an offset past the end of A: the buffer
+  // load returns zeros without touching memory; those rows are never stored.)
+  auto gather_finish = [&](const MxTileInfo& ti, const int* raw, uint32_t* adma, uint32_t* aoff) {
     uint32_t arow[NRAW];
 #pragma unroll
     for (int j = 0; j < NRAW; ++j)
       arow[j] = g.gather ? (uint32_t)min(max(raw[j], 0) / g.topk, g.total_rows / g.topk - 1)
                          : (uint32_t)raw[j];
 #pragma unroll
-    for (int i = 0; i < C::LPA; ++i)
-      adma[i] = arow[i] * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+    for (int i = 0; i < C::LPA; ++i) {
+      const bool pad = 8 * (wave + C::NW * i) + (lane >> 3) >= ti.nrows;
+      adma[i] = pad ? (uint32_t)arows_total * (uint32_t)K
+                    : arow[i] * (uint32_t)K + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+    }
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) aoff[mi] = arow[C::LPA + mi] * (uint32_t)(K / 32);
   };
@@ -329,7 +334,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
   // first tile: its rows, then stage 0, its first scale quad and stages 1..3
   // (the order in which the last quad of a tile starts the next one)
   gather_issue(cur, nxt_raw);
-  gather_finish(nxt_raw, cur_adma, cur_aoff);
+  gather_finish(cur, nxt_raw, cur_adma, cur_aoff);
   issue(cur, cur_adma, 0, 0);
   load_scales(cur, cur_aoff, 0);
 #pragma unroll
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void ffn_mx_tiled(GroupedGemm g, i
       next_quad_scales();
     }
     kt_base = 4 * c_cur;
-    gather_finish(nxt_raw, nxt_adma, nxt_aoff);
+    gather_finish(nxt, nxt_raw, nxt_adma, nxt_aoff);
     step(acc, I0{}, Last{});
     step(acc, I1{}, Last{});
     step(acc, I2{}, Last{});
