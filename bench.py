@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen3_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the second timing of the layer replayed from a captured HIP graph")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -139,7 +141,7 @@ def summarize_counters(config, fetch_csv, write_csv, copy_fetch_csv, copy_write_
     kib = 1024 * 1024  # the copy moves 1 GiB = 1,048,576 KiB each way
     sf, sw = kib / cf, kib / cw
     cfg_arg = "" if config == "qwen3_decode" else f" --config {config}"
-    run = f"python $R/bench.py{cfg_arg} --steps 5 --warmup 2 --no-cpu-baseline"
+    run = f"python $R/bench.py{cfg_arg} --steps 5 --warmup 2 --no-cpu-baseline --no-graph"
     lines = [f"# HBM byte counters, {COUNTER_TITLES.get(config, config)}", "",
              "Each counter in its own pass (run from /tmp on one MI355X, repo at $R):", "", "```",
              f"rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE_{config} -o run --output-format csv -- {run}",
@@ -389,6 +391,36 @@ def bench_norm(args):
     print(json.dumps(res), flush=True)
 
 
+def time_graph_replay(layer, x, out, K, Wm):
+    """The layer step captured once into a HIP graph (the library reads no
+    device value on the host, so one capture serves every step) and replayed:
+    W untimed replays, then K replays bracketed by device synchronisations.
+    Every replay must reproduce the eager output bit for bit."""
+    import torch
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(x, out)  # a first call on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(x, out)
+    for _ in range(Wm):
+        g.replay()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {K} graph replays")
+    t0 = time.perf_counter()
+    for _ in range(K):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    if not torch.equal(out, eager):
+        raise RuntimeError("graph replay output differs from the eager step")
+    del g
+    return {"ms_per_step": round(ms, 5), "matches_eager": True}
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -449,6 +481,8 @@ def main():
     g1_ms = sum(a.elapsed_ms(b) for a, b in ev) / K
     ms = elapsed * 1e3 / K
 
+    graph = None if args.no_graph else time_graph_replay(layer, x, out, K, Wm)
+
     counts = layer.buf["counts"].cpu().numpy()
     wl = workload_bytes_flops(cfg, counts)
     decode = cfg.T * cfg.k <= 16 * cfg.E
@@ -489,6 +523,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu_b,
     }
+    if graph is not None:
+        res["graph"] = dict(graph, tokens_per_s=round(cfg.T / (graph["ms_per_step"] * 1e-3), 1))
     print(json.dumps(res), flush=True)
 
 
