@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the second timing of the layer replayed from a captured HIP graph")
+    ap.add_argument("--cold-steps", type=int, default=0,
+                    help="also time this many steps with a 512 MiB read before each one (L2 and "
+                         "Infinity Cache evicted), by HIP events around each step")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -464,6 +467,8 @@ def main():
 
     K, Wm = args.steps, args.warmup
     ev = [(TimingEvent(), TimingEvent()) for _ in range(K)]
+    ev_step = [(TimingEvent(), TimingEvent()) for _ in range(K)]
+    stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
 
     log(f"[bench] warm-up {Wm} steps")
@@ -474,12 +479,38 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         layer.time_ffn_up(*ev[i])
+        ev_step[i][0].record(stream)
         layer.forward(x, out)
+        ev_step[i][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     layer.time_ffn_up(None, None)
     g1_ms = sum(a.elapsed_ms(b) for a, b in ev) / K
     ms = elapsed * 1e3 / K
+    step_ms = sorted(a.elapsed_ms(b) for a, b in ev_step)
+
+    cold = None
+    if args.cold_steps > 0:
+        # each step after a read of 512 MiB (outside its events): the touched
+        # weights come from HBM, not from a cache the previous step filled.
+        # A read, not a write: a written buffer leaves the Infinity Cache
+        # full of dirty lines whose write-back the timed step would pay for.
+        flush = torch.ones(64 << 20, dtype=torch.int64, device="cuda")
+        sink = torch.empty(1, dtype=torch.int64, device="cuda")
+        for _ in range(3):
+            torch.sum(flush, dim=0, keepdim=True, out=sink)
+        torch.cuda.synchronize()
+        ev_cold = [(TimingEvent(), TimingEvent()) for _ in range(args.cold_steps)]
+        for a, b in ev_cold:
+            torch.sum(flush, dim=0, keepdim=True, out=sink)
+            a.record(stream)
+            layer.forward(x, out)
+            b.record(stream)
+        torch.cuda.synchronize()
+        c = sorted(a.elapsed_ms(b) for a, b in ev_cold)
+        cold = {"steps": args.cold_steps, "median_ms": round(c[len(c) // 2], 5), "min_ms": round(c[0], 5),
+                "flush_read_bytes": 512 << 20}
+        del flush
 
     graph = None if args.no_graph else time_graph_replay(layer, x, out, K, Wm)
 
@@ -523,6 +554,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu_b,
     }
+    res["step_ms"] = {"median": round(step_ms[K // 2], 5), "min": round(step_ms[0], 5),
+                      "source": "HIP events around each timed step"}
+    if cold is not None:
+        res["cold"] = cold
     if graph is not None:
         res["graph"] = dict(graph, tokens_per_s=round(cfg.T / (graph["ms_per_step"] * 1e-3), 1))
     print(json.dumps(res), flush=True)
