@@ -60,7 +60,7 @@ constexpr int RP_HS = 256;
 // the tiles alone would leave CUs idle (about 2048 blocks in flight), ks a
 // power of two dividing the H/32 K-steps; the ks partial tiles are summed in
 // order by router_reduce.
-constexpr int RM_TT = 32, RM_TE = 64;
+constexpr int RM_TT = 128, RM_TE = 64;
 
 static int router_ksplit(int T, int H, int E) {
   const long long tiles = (long long)((T + RM_TT - 1) / RM_TT) * ((E + RM_TE - 1) / RM_TE);
@@ -173,82 +173,115 @@ __global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ p
   logits[i] = sum_slices(partial + i, S, (size_t)T * E);
 }
 
-// Many tokens (prefill): block tile 32 tokens x 64 experts, K step 32,
-// operands staged in double-buffered LDS (the split is done once, by the
-// loading thread); wave w owns experts 16w..16w+15 of the tile and both
-// 16-token halves (6 MFMAs per K step).  Block z of gridDim.z covers the
-// z-th 1/gridDim.z of K and writes its partial tile to logits + z*T*E.
+// Many tokens (prefill): block tile 128 tokens x 64 experts, stages of KS
+// K-steps of 32 in double-buffered LDS (the split is done once per block and
+// stage, by the loading thread, and serves all 128 tokens); wave w owns
+// tokens 32w..32w+31 of the tile (two 16-token fragments) and all 64 experts
+// (four 16-expert groups x three parts: 24 MFMAs per K step).  Each
+// accumulator takes its K-steps in order, the three parts of a step in the
+// order hi, mid, lo, whatever KS is.  Block z of gridDim.z covers the z-th
+// 1/gridDim.z of K and writes its partial tile to logits + z*T*E.
 
+template <int KS>
 __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wr, int T,
                                                           int H, int E,
                                                           float* __restrict__ logits) {
-  __shared__ u32x4 xs[2][RM_TT * 4];
-  __shared__ u32x4 ws[2][3][RM_TE * 4];
+  __shared__ u32x4 xs[2][KS][RM_TT * 4];
+  __shared__ u32x4 ws[2][KS][3][RM_TE * 4];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * RM_TT, e0 = blockIdx.y * RM_TE;
-  const int nk = H / 32 / (int)gridDim.z, kbeg = (int)blockIdx.z * nk * 32;
+  const int nk = H / (32 * KS) / (int)gridDim.z, kbeg = (int)blockIdx.z * nk * 32 * KS;
   logits += (size_t)blockIdx.z * T * E;
-  // loaders: threads 0..127 -> x (token tid/4, chunk tid%4); all -> wr (expert tid/4, chunk tid%4)
+  // loaders: thread -> x rows tid/4 and 64 + tid/4, wr row (expert) tid/4;
+  // 16-byte chunk tid%4 of each 32 columns of the stage (rows past T or E
+  // reuse a valid row; their results are not stored)
   const int lrow = tid >> 2, lch = tid & 3;
-  const uint16_t* xp = x + (size_t)min(t0 + (lrow & 31), T - 1) * H + kbeg + lch * 8;
+  const uint16_t* xp0 = x + (size_t)min(t0 + lrow, T - 1) * H + kbeg + lch * 8;
+  const uint16_t* xp1 = x + (size_t)min(t0 + 64 + lrow, T - 1) * H + kbeg + lch * 8;
   const float* wp = wr + (size_t)min(e0 + lrow, E - 1) * H + kbeg + lch * 8;
-  // two register sets: step k+2 is loaded while step k computes and step k+1
-  // waits to be split and stored into the other LDS buffer
-  u32x4 rx0, rx1;
-  float rw0[8], rw1[8];
-  auto gload = [&](u32x4& rx, float* rw, int k0) {
-    if (tid < 128) rx = ld16(xp + k0);
-    const float4 a = *reinterpret_cast<const float4*>(wp + k0);
-    const float4 b = *reinterpret_cast<const float4*>(wp + k0 + 4);
-    rw[0] = a.x; rw[1] = a.y; rw[2] = a.z; rw[3] = a.w;
-    rw[4] = b.x; rw[5] = b.y; rw[6] = b.z; rw[7] = b.w;
+  struct Regs {
+    u32x4 xa[KS], xb[KS];
+    float w[KS][8];
   };
-  auto lstore = [&](const u32x4& rx, const float* rw, int buf) {
-    if (tid < 128) xs[buf][lrow * 4 + lch] = rx;
-    u32x4 h, m, l;
-    split3_bf16(rw, h, m, l);
-    ws[buf][0][lrow * 4 + lch] = h;
-    ws[buf][1][lrow * 4 + lch] = m;
-    ws[buf][2][lrow * 4 + lch] = l;
+  // two register sets: stage k+2 is loaded while stage k computes and stage
+  // k+1 waits to be split and stored into the other LDS buffer
+  Regs r0, r1;
+  auto gload = [&](Regs& r, int k0) {
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      const int k = k0 + 32 * j;
+      r.xa[j] = ld16(xp0 + k);
+      r.xb[j] = ld16(xp1 + k);
+      const float4 a = *reinterpret_cast<const float4*>(wp + k);
+      const float4 b = *reinterpret_cast<const float4*>(wp + k + 4);
+      r.w[j][0] = a.x; r.w[j][1] = a.y; r.w[j][2] = a.z; r.w[j][3] = a.w;
+      r.w[j][4] = b.x; r.w[j][5] = b.y; r.w[j][6] = b.z; r.w[j][7] = b.w;
+    }
   };
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  auto lstore = [&](const Regs& r, int buf) {
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      xs[buf][j][lrow * 4 + lch] = r.xa[j];
+      xs[buf][j][(64 + lrow) * 4 + lch] = r.xb[j];
+      u32x4 h, m, l;
+      split3_bf16(r.w[j], h, m, l);
+      ws[buf][j][0][lrow * 4 + lch] = h;
+      ws[buf][j][1][lrow * 4 + lch] = m;
+      ws[buf][j][2][lrow * 4 + lch] = l;
+    }
+  };
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) acc[mi][g] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fc = lane >> 4;
   auto compute = [&](int buf) {
-    const u32x4 a0 = xs[buf][fr * 4 + fc];
-    const u32x4 a1 = xs[buf][(16 + fr) * 4 + fc];
 #pragma unroll
-    for (int sp = 0; sp < 3; ++sp) {
-      const u32x4 b = ws[buf][sp][(16 * wave + fr) * 4 + fc];
-      acc0 = mfma16x16x32(a0, b, acc0);
-      acc1 = mfma16x16x32(a1, b, acc1);
+    for (int j = 0; j < KS; ++j) {
+      const u32x4 a0 = xs[buf][j][(32 * wave + fr) * 4 + fc];
+      const u32x4 a1 = xs[buf][j][(32 * wave + 16 + fr) * 4 + fc];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) {
+          const u32x4 b = ws[buf][j][sp][(16 * g + fr) * 4 + fc];
+          acc[0][g] = mfma16x16x32(a0, b, acc[0][g]);
+          acc[1][g] = mfma16x16x32(a1, b, acc[1][g]);
+        }
     }
   };
-  gload(rx0, rw0, 0);
-  if (nk > 1) gload(rx1, rw1, 32);
-  lstore(rx0, rw0, 0);
+  constexpr int KW = 32 * KS;  // columns per stage
+  gload(r0, 0);
+  if (nk > 1) gload(r1, KW);
+  lstore(r0, 0);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
-    if (kt + 2 < nk) gload(rx0, rw0, (kt + 2) * 32);
+    if (kt + 2 < nk) gload(r0, (kt + 2) * KW);
     compute(0);
-    if (kt + 1 < nk) lstore(rx1, rw1, 1);
+    if (kt + 1 < nk) lstore(r1, 1);
     __syncthreads();
     if (kt + 1 >= nk) break;
-    if (kt + 3 < nk) gload(rx1, rw1, (kt + 3) * 32);
+    if (kt + 3 < nk) gload(r1, (kt + 3) * KW);
     compute(1);
-    if (kt + 2 < nk) lstore(rx0, rw0, 0);
+    if (kt + 2 < nk) lstore(r0, 0);
     __syncthreads();
   }
-  // D[m][n]: lane holds expert 16*wave + (lane & 15), tokens 4*(lane>>4) + i
-  const int e = e0 + 16 * wave + fr;
-  if (e < E) {
+  // D[m][n]: lane holds expert 16*g + (lane & 15), tokens 16*mi + 4*(lane>>4) + i
+  // of the wave's 32
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ta = t0 + 4 * fc + i, tb = t0 + 16 + 4 * fc + i;
-      if (ta < T) logits[(size_t)ta * E + e] = acc0[i];
-      if (tb < T) logits[(size_t)tb * E + e] = acc1[i];
-    }
+  for (int g = 0; g < 4; ++g) {
+    const int e = e0 + 16 * g + fr;
+    if (e >= E) continue;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 32 * wave + 16 * mi + 4 * fc + i;
+        if (t < T) logits[(size_t)t * E + e] = acc[mi][g][i];
+      }
   }
 }
 
@@ -353,9 +386,14 @@ int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E
                        T, E, logits);
   } else {
     const int ks = router_ksplit(T, H, E);
-    hipLaunchKernelGGL(router_logits_mfma,
-                       dim3((T + RM_TT - 1) / RM_TT, (E + RM_TE - 1) / RM_TE, ks), dim3(256), 0, s,
-                       x, wr, T, H, E, ks > 1 ? ws : logits);
+    const dim3 grid((T + RM_TT - 1) / RM_TT, (E + RM_TE - 1) / RM_TE, ks);
+    float* dst = ks > 1 ? ws : logits;
+    // two 32-column steps per stage when every block's K range holds an
+    // even number of them (the same sums either way)
+    if ((H / 32 / ks) % 2 == 0)
+      hipLaunchKernelGGL(router_logits_mfma<2>, grid, dim3(256), 0, s, x, wr, T, H, E, dst);
+    else
+      hipLaunchKernelGGL(router_logits_mfma<1>, grid, dim3(256), 0, s, x, wr, T, H, E, dst);
     if (ks > 1)
       hipLaunchKernelGGL(router_reduce, dim3((T * E + 255) / 256), dim3(256), 0, s, ws, ks, T, E,
                          logits);

@@ -59,10 +59,11 @@ def test_router_logits_checks(lib):
     ws = lib.moe_router_workspace_size(4, 256, 8)
     assert ws == 1 * 4 * 8 * 4                                   # one 256-wide slice of partials
     assert lib.moe_router_workspace_size(4, 4096, 128) == 16 * 4 * 128 * 4
-    # many tokens: K split over 8 blocks per 32x64 tile while that keeps <= 2048 blocks
+    # many tokens: K split over up to 8 blocks per 128x64 tile while that keeps <= 2048 blocks
     assert lib.moe_router_workspace_size(65, 4096, 128) == 8 * 65 * 128 * 4
     assert lib.moe_router_workspace_size(4096, 4096, 128) == 8 * 4096 * 128 * 4
-    assert lib.moe_router_workspace_size(4096, 4096, 192) == 4 * 4096 * 192 * 4
+    assert lib.moe_router_workspace_size(4096, 4096, 192) == 8 * 4096 * 192 * 4
+    assert lib.moe_router_workspace_size(32768, 4096, 128) == 4 * 32768 * 128 * 4  # 512 tiles
     assert lib.moe_router_workspace_size(65536, 4096, 256) == 0     # enough tiles: no split
     assert f(None, FAKE, 4, 256, 8, FAKE, FAKE, ws, None) == NULL
     assert f(FAKE, FAKE, 4, 255, 8, FAKE, FAKE, ws, None) == UNSUP        # H % 256
