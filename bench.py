@@ -146,11 +146,11 @@ def summarize_counters(config, fetch_csv, write_csv, copy_fetch_csv, copy_write_
     cfg_arg = "" if config == "qwen3_decode" else f" --config {config}"
     run = f"python $R/bench.py{cfg_arg} --steps 5 --warmup 2 --no-cpu-baseline --no-graph"
     lines = [f"# HBM byte counters, {COUNTER_TITLES.get(config, config)}", "",
-             "Each counter in its own pass (run from /tmp on one MI355X, repo at $R):", "", "```",
-             f"rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE_{config} -o run --output-format csv -- {run}",
-             f"rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_WRITE_SIZE_{config} -o run --output-format csv -- {run}",
-             "rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
-             "rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_WRITE_SIZE_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
+             "Each counter in its own pass (run from /tmp on one MI355X, repo at $R, output under $OUT):", "", "```",
+             f"rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_{config} -o run --output-format csv -- {run}",
+             f"rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_{config} -o run --output-format csv -- {run}",
+             "rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
+             "rocprofv3 --pmc WRITE_SIZE -d $OUT/pmc_WRITE_SIZE_copy -o run --output-format csv -- python $R/bench.py --calibrate-copy-mib 1024",
              f"python $R/bench.py --config {config} --summarize-counters <the four run_counter_collection.csv files>",
              "```", "",
              f"Calibration (1 GiB device copy): FETCH_SIZE {cf:,.1f} KiB -> scale x{sf:.3f}; "
