@@ -1,0 +1,66 @@
+"""Host-side logic of bench.py: the algorithmic bytes and flops that the
+roofline fractions divide by, pinned to figures derived by hand from the
+layer shapes (expert weight sizes, router weight, x in and out, 2 flops per
+multiply-add of the three expert projections), and the refusal of more than
+one GPU.  No GPU needed."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from expert_routing_grouped_gate_amd import workloads as W  # noqa: E402
+
+
+def counts_touching(E, n):
+    c = np.zeros(E, dtype=np.int32)
+    c[:n] = 1
+    return c
+
+
+def test_bf16_decode_bytes():
+    # per expert: w13 2 x 1536 x 4096 bf16 + w2 4096 x 1536 bf16 = 37,748,736 B;
+    # plus the fp32 router weight (2 MiB) and x in + out (2 x 16 x 4096 x 2 B)
+    w = bench.workload_bytes_flops(W.CONFIGS["qwen3_decode"], counts_touching(128, 80))
+    assert w["n_touched"] == 80
+    assert w["layer_bytes"] == 80 * 37_748_736 + 128 * 4096 * 4 + 2 * 16 * 4096 * 2
+    assert w["flops"] == 2 * 16 * 8 * 3 * 1536 * 4096          # 4.83 GFLOP
+    # GEMM1: the touched w13 slices, x, and the bf16 activations it writes
+    assert w["g1_bytes"] == 80 * 25_165_824 + 16 * 4096 * 2 + 16 * 8 * 1536 * 2
+    assert w["g1_flops"] == 2 * 16 * 8 * 2 * 1536 * 4096
+
+
+def test_prefill_flops():
+    w = bench.workload_bytes_flops(W.CONFIGS["qwen3_prefill"], counts_touching(128, 128))
+    assert w["flops"] == 1_236_950_581_248                         # 1.2370 TFLOP
+    assert w["g1_flops"] == 824_633_720_832                         # 824.6 GFLOP
+    assert w["layer_bytes"] == 128 * 37_748_736 + 128 * 4096 * 4 + 2 * 4096 * 4096 * 2
+
+
+def test_hy3_adds_the_shared_expert_and_bias():
+    w = bench.workload_bytes_flops(W.CONFIGS["hy3"], counts_touching(192, 155))
+    shared = 3 * 1536 * 4096 * 2
+    assert w["layer_bytes"] == (155 * 37_748_736 + shared + 192 * 4096 * 4 + 192 * 4
+                                + 2 * 4096 * 4096 * 2)
+    assert w["flops"] == 1_236_950_581_248 + 2 * 4096 * 3 * 1536 * 4096   # 1.3916 TFLOP
+
+
+def test_w4a8_bytes():
+    # per expert: E2M1 codes (half a byte each) + one E8M0 scale per 32 values:
+    # w13 6,291,456 + 393,216 B, w2 3,145,728 + 196,608 B = 10,027,008 B
+    cfg = W.CONFIGS["qwen3_decode_w4a8"]
+    w = bench.workload_bytes_flops(cfg, counts_touching(128, 42))
+    assert w["layer_bytes"] == 42 * 10_027_008 + 128 * 4096 * 4 + 128 * 4 + 2 * 16 * 4096 * 2
+    # GEMM1 writes MXFP8 activations: one byte per value + one scale per 32
+    assert w["g1_bytes"] == 42 * (6_291_456 + 393_216) + 16 * 4096 * 2 + 16 * 8 * (1536 + 48)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
