@@ -465,11 +465,10 @@ int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t*
       return st;
   } else {
     if (mx && (st = moe_mx_quantize(x, T, d->H, b->xq, b->xq_scales, stream))) return st;
-    if ((st = moe_router_logits(x, d->wr, T, d->H, d->E, b->logits, b->workspace,
-                                b->workspace_bytes, stream)))
-      return st;
-    if ((st = moe_gate_topk(b->logits, d->bias, T, d->E, k, d->gate_mode, d->routed_scale,
-                            d->eps, b->topk_ids, b->topk_w, stream)))
+    // router and gate (the router's slice partials are summed inside the gate)
+    if ((st = moe::launch_router_gate(x, d->wr, T, d->H, d->E, k, d->gate_mode, d->routed_scale,
+                                      d->eps, d->bias, b->logits, b->topk_ids, b->topk_w,
+                                      static_cast<float*>(b->workspace), as_stream(stream))))
       return st;
     if ((st = moe_route(b->topk_ids, T, k, d->E, b->counts, b->offsets, b->sorted_pair,
                         b->pair_pos, b->dev_status, b->workspace, b->workspace_bytes, stream)))

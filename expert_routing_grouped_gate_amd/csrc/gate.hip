@@ -378,26 +378,33 @@ int launch_router_partial(const uint16_t* x, const float* wr, int T, int H, int 
   return launch_status();
 }
 
-int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
-                         float* ws, hipStream_t s) {
+// The partial-sum kernels of S1: returns the number S of slice partials
+// written to ws ([S, T, E], summed in slice order afterwards), or 0 when the
+// logits were written directly.
+static int launch_router_slices(const uint16_t* x, const float* wr, int T, int H, int E,
+                                float* logits, float* ws, hipStream_t s) {
   if (T <= 64) {
     launch_router_partial(x, wr, T, H, E, ws, nullptr, nullptr, s);
-    hipLaunchKernelGGL(router_reduce, dim3((T * E + 255) / 256), dim3(256), 0, s, ws, H / RP_HS,
-                       T, E, logits);
-  } else {
-    const int ks = router_ksplit(T, H, E);
-    const dim3 grid((T + RM_TT - 1) / RM_TT, (E + RM_TE - 1) / RM_TE, ks);
-    float* dst = ks > 1 ? ws : logits;
-    // two 32-column steps per stage when every block's K range holds an
-    // even number of them (the same sums either way)
-    if ((H / 32 / ks) % 2 == 0)
-      hipLaunchKernelGGL(router_logits_mfma<2>, grid, dim3(256), 0, s, x, wr, T, H, E, dst);
-    else
-      hipLaunchKernelGGL(router_logits_mfma<1>, grid, dim3(256), 0, s, x, wr, T, H, E, dst);
-    if (ks > 1)
-      hipLaunchKernelGGL(router_reduce, dim3((T * E + 255) / 256), dim3(256), 0, s, ws, ks, T, E,
-                         logits);
+    return H / RP_HS;
   }
+  const int ks = router_ksplit(T, H, E);
+  const dim3 grid((T + RM_TT - 1) / RM_TT, (E + RM_TE - 1) / RM_TE, ks);
+  float* dst = ks > 1 ? ws : logits;
+  // two 32-column steps per stage when every block's K range holds an even
+  // number of them (the same sums either way)
+  if ((H / 32 / ks) % 2 == 0)
+    hipLaunchKernelGGL(router_logits_mfma<2>, grid, dim3(256), 0, s, x, wr, T, H, E, dst);
+  else
+    hipLaunchKernelGGL(router_logits_mfma<1>, grid, dim3(256), 0, s, x, wr, T, H, E, dst);
+  return ks > 1 ? ks : 0;
+}
+
+int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
+                         float* ws, hipStream_t s) {
+  const int S = launch_router_slices(x, wr, T, H, E, logits, ws, s);
+  if (S > 0)
+    hipLaunchKernelGGL(router_reduce, dim3((T * E + 255) / 256), dim3(256), 0, s, ws, S, T, E,
+                       logits);
   return launch_status();
 }
 
@@ -584,6 +591,28 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
                         wout + (size_t)t * k);
 }
 
+// S1's last step fused into S2: wave t sums token t's slice partials (the
+// summation of router_reduce, so the logits are the same bits), stores them
+// and runs the gate; saves a launch and a round trip of the logits.
+template <int MODE, int NSL>
+__global__ __launch_bounds__(256) void gate_topk_slices_kernel(
+    const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E, int k,
+    float routed_scale, float eps, float* __restrict__ logits, int32_t* __restrict__ ids,
+    float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // wave-uniform; no barriers
+  float L[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    L[i] = e < E ? sum_slices(partial + (size_t)t * E + e, S, (size_t)T * E) : 0.f;
+    if (e < E) logits[(size_t)t * E + e] = L[i];
+  }
+  gate_token<MODE, NSL>(L, bias, E, k, routed_scale, eps, ids + (size_t)t * k,
+                        wout + (size_t)t * k);
+}
+
 // --------------------------------------------------- S1+S2+S3/S4, decode ---
 // Few tokens (T <= 16, T*k <= 1024): one block of 1024 threads finishes the
 // routing in one launch after router_partial.  Wave t sums token t's slice
@@ -721,6 +750,28 @@ struct GateTopk {
                        bias, T, E, k, routed_scale, eps, ids, w);
   }
 };
+
+template <int MODE, int NSL>
+struct GateTopkSlices {
+  static void run(hipStream_t s, const float* partial, int S, const float* bias, int T, int E,
+                  int k, float routed_scale, float eps, float* logits, int32_t* ids, float* w) {
+    hipLaunchKernelGGL((gate_topk_slices_kernel<MODE, NSL>), dim3((T + 3) / 4), dim3(256), 0, s,
+                       partial, S, bias, T, E, k, routed_scale, eps, logits, ids, w);
+  }
+};
+
+int launch_router_gate(const uint16_t* x, const float* wr, int T, int H, int E, int k, int mode,
+                       float routed_scale, float eps, const float* bias, float* logits,
+                       int32_t* ids, float* w, float* ws, hipStream_t s) {
+  const int S = launch_router_slices(x, wr, T, H, E, logits, ws, s);
+  if (S > 0)
+    by_mode_slots<GateTopkSlices>(mode, E, s, static_cast<const float*>(ws), S, bias, T, E, k,
+                                  routed_scale, eps, logits, ids, w);
+  else
+    by_mode_slots<GateTopk>(mode, E, s, static_cast<const float*>(logits), bias, T, E, k,
+                            routed_scale, eps, ids, w);
+  return launch_status();
+}
 
 int launch_gate_route_small(const float* partial, int H, const float* bias, int T, int E, int k,
                             int mode, float routed_scale, float eps, float* logits, int32_t* ids,

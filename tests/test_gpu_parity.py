@@ -243,11 +243,15 @@ def test_layer_small(name):
     _layer_check(SMALL[name])
 
 
-@pytest.mark.parametrize("name", ["tiny", "small_hy3_decode", "wide_k_decode"])
-def test_decode_front_end_equals_the_step_calls(name):
-    """With T <= 16 the layer routes with two launches (router partial sums,
-    then one block for logits, top-k, counts and permutation); its buffers
-    must equal the standalone router, gate and route calls bit for bit."""
+@pytest.mark.parametrize("name", ["tiny", "small_hy3_decode", "wide_k_decode", "wide_k", "small_hy3",
+                                  "small_prefill", "tiled4_stream"])
+def test_layer_routing_equals_the_step_calls(name):
+    """The layer's own routing launches must equal the standalone router,
+    gate and route calls bit for bit: with T <= 16 the router partial sums,
+    then one block for logits, top-k, counts and permutation; with more
+    tokens the router's slice partials summed inside the gate (one slice at
+    H = 256 and T <= 64, eight K-split tiles of one- or two-step stages
+    above)."""
     L = get_layer(SMALL[name])
     cfg = L.cfg
     layer = L.layer()
