@@ -56,10 +56,10 @@ __device__ __forceinline__ void split3_bf16(const float* w8, u32x4& hi, u32x4& m
 // path needs no separate quantiser launch.
 constexpr int RP_HS = 256;
 
-// Many tokens: the MFMA router splits K over ks blocks per output tile when
-// the tiles alone would leave CUs idle (about 2048 blocks in flight), ks a
-// power of two dividing the H/32 K-steps; the ks partial tiles are summed in
-// order by router_reduce.
+// Many tokens: the MFMA router splits K over ks <= 8 blocks per output tile
+// while that keeps the grid within 2048 blocks, ks a power of two dividing
+// the H/32 K-steps; the ks partial tiles are summed in order by
+// router_reduce, or inside the gate when the layer routes.
 constexpr int RM_TT = 128, RM_TE = 64;
 
 static int router_ksplit(int T, int H, int E) {
