@@ -279,7 +279,7 @@ __device__ __forceinline__ void mx_store(const GroupedGemm& g, const MxTile& t, 
 
 // At most 168 registers: three waves per SIMD, so that a decode layer's
 // tiles (touched experts x column tiles, ~2,000-2,700) need about one wave each.
-template <bool SWIGLU, int U>
+template <bool SWIGLU, int U, int D>
 __global__ __launch_bounds__(256, 3) void ffn_mx_stream(GroupedGemm g, int n_tiles) {
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, kb = lane >> 4;
@@ -295,6 +295,42 @@ __global__ __launch_bounds__(256, 3) void ffn_mx_stream(GroupedGemm g, int n_til
   if (gw >= total) return;  // the kernel has no barriers
   const int nb = g.K / 128 / U;
   MxTile cur = mx_tile_at<SWIGLU>(g, tm, gw, li, kb);
+  if constexpr (D == 3) {
+    // three register batches in rotation (nb % 3 == 0): batches j+1 and j+2
+    // are in flight while batch j computes; the last two loads of a tile
+    // fetch the next tile's batches 0 and 1, so every tile starts with both
+    // loaded
+    MxBatch<U> b0, b1, b2;
+    mx_load<SWIGLU, U>(b0, g, cur, 0, lane);
+    mx_load<SWIGLU, U>(b1, g, cur, U, lane);
+    for (int id = gw; id < total; id += nw) {
+      MxTile nxt = cur;
+      if (id + nw < total)
+        nxt = mx_tile_at<SWIGLU>(g, tm, id + nw, li, kb);
+      else
+        nxt.live = 0;  // the batches loaded past the last tile read nothing
+      f32x4 acc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < nb; b += 3) {
+        mx_load<SWIGLU, U>(b2, g, b + 2 < nb ? cur : nxt, b + 2 < nb ? (b + 2) * U : (b + 2 - nb) * U, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_compute<U>(b0, acc, kb);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_load<SWIGLU, U>(b0, g, b + 3 < nb ? cur : nxt, b + 3 < nb ? (b + 3) * U : (b + 3 - nb) * U, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_compute<U>(b1, acc, kb);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_load<SWIGLU, U>(b1, g, b + 4 < nb ? cur : nxt, b + 4 < nb ? (b + 4) * U : (b + 4 - nb) * U, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mx_compute<U>(b2, acc, kb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mx_store<SWIGLU>(g, cur, acc, li, kb);
+      cur = nxt;
+    }
+    return;
+  }
   MxBatch<U> b0, b1;
   mx_load<SWIGLU, U>(b0, g, cur, 0, lane);
   for (int id = gw; id < total; id += nw) {
@@ -338,10 +374,10 @@ static inline bool mx_matrix_fits(const GroupedGemm& g, bool swiglu) {
   return rows * (g.K / 2) < (1ll << 31);
 }
 
-template <bool SWIGLU, int U>
+template <bool SWIGLU, int U, int D = 2>
 static void launch_mx_stream(const GroupedGemm& g, hipStream_t s) {
   const int nt = g.N / (SWIGLU ? 32 : 64);
-  auto k = ffn_mx_stream<SWIGLU, U>;
+  auto k = ffn_mx_stream<SWIGLU, U, D>;
   const int grid = resident_grid(reinterpret_cast<const void*>(k), 256, (mx_tiles_bound(g, nt) + 3) / 4);
   hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, g, nt);
 }
@@ -367,6 +403,8 @@ int launch_ffn_down_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (!mx_matrix_fits(g, false)) return -3;  // MOE_ERR_UNSUPPORTED
   if (!small_m && mx_tiled_fits(g, false))
     launch_mx_tiled(g, false, s);
+  else if ((g.K / 128) % 3 == 0)
+    launch_mx_stream<false, 1, 3>(g, s);
   else
     launch_mx_stream<false, 1>(g, s);
   return launch_status();
