@@ -395,10 +395,12 @@ int launch_ffn_up_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s) {
   return launch_status();
 }
 
-// K = I (a multiple of 128); N = H (a multiple of 64).  Single-step batches:
-// with K = 1536 a tile is only 12 steps, and the smaller register set (four
-// waves per SIMD) measured faster than two-step batches (decode layer
-// 102.6 -> 100.9 us together with the register bound above).
+// K = I (a multiple of 128); N = H (a multiple of 64).  Single-step batches
+// (a tile is only 12 steps at K = 1536).  When the step count is a multiple
+// of 3 (I = 1536), three batches rotate (two in flight while one computes;
+// 148 registers, three waves per SIMD); otherwise two batches (120
+// registers, four waves per SIMD).  Many rows per expert and K a multiple of
+// 512: the LDS-tiled kernel.
 int launch_ffn_down_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s) {
   if (!mx_matrix_fits(g, false)) return -3;  // MOE_ERR_UNSUPPORTED
   if (!small_m && mx_tiled_fits(g, false))

@@ -361,3 +361,76 @@ def test_w4a8_layer_path_quantises_x_and_activation():
     d = np.abs(res8["out"] - res16["out"])
     assert d.max() <= 0.15 * np.abs(res16["out"]).max()
     assert d.max() > 0   # the activation really was requantised
+
+
+# ------------------------------------------- W4A8 quantisation points ------
+
+def _quant_points():
+    with open(os.path.join(GOLDEN, "w4a8_quant_points_handworked.json")) as f:
+        return json.load(f)
+
+
+def test_w4a8_swiglu_output_quantised_as_one_value():
+    """Hand-worked: the SwiGLU output a = SiLU(g) * u is quantised to MXFP8
+    along I as one value (not g and u apart, not after a bf16 rounding)."""
+    case = _quant_points()["swiglu_output"]
+    I, H = 32, 33
+    w13 = np.zeros((2 * I, H))
+    w13[:I, 32] = 48.0                 # gate: g_j = 48 * x_32 = 48
+    w13[I:, :I] = np.eye(I)            # up:   u_j = p_j
+    w2 = np.zeros((H, I))
+    w2[:I] = np.eye(I)
+    assert float(moe.silu(48.0)) == 48.0
+    for row in case["rows"]:
+        x = np.zeros((1, H))
+        x[0, :len(row["p"])] = row["p"]
+        x[0, 32] = 1.0
+        y = moe.expert_ffn(x, w13, w2, act="mxfp8")
+        want = np.zeros(H)
+        want[:len(row["y"])] = row["y"]
+        np.testing.assert_array_equal(y[0], want)
+
+
+def test_w4a8_shared_expert_runs_on_quantised_x():
+    """Hand-worked: in the W4A8 layer the shared expert takes the MXFP8 x,
+    as the routed experts do; zero routed experts leave only its row."""
+    case = _quant_points()["shared_on_quantised_x"]
+    H, I, E = 64, 32, 2
+    zero = (np.zeros((2 * I, H)), np.zeros((H, I)))
+    s13 = np.zeros((2 * I, H))
+    s13[:I, 32] = 48.0
+    s13[I:, :I] = np.eye(I)
+    s2 = np.zeros((H, I))
+    s2[:I] = np.eye(I)
+    rows = case["rows"]
+    x = np.zeros((len(rows), H))
+    for t, row in enumerate(rows):
+        x[t, :len(row["p"])] = row["p"]
+        x[t, 32] = 1.0
+    wr = np.zeros((E, H), dtype=np.float32)
+    res = moe.layer_forward(x, wr, 1, "softmax", lambda e: zero, E, shared_weights=(s13, s2), fmt="w4a8")
+    assert res["ids"].ravel().tolist() == [0] * len(rows)   # tied logits -> lower id
+    for t, row in enumerate(rows):
+        want = np.zeros(H)
+        want[:len(row["out"])] = row["out"]
+        np.testing.assert_array_equal(res["out"][t], want)
+
+
+def test_bf16_round_subnormals():
+    """The bf16 subnormal range (|a| < 2^-126, grid q = 2^-133): hand-worked
+    ties to even, the carry into the smallest normal, and fp32-exact random
+    values against torch's bf16 cast."""
+    q = 2.0 ** -133
+    cases = {1.0: 1.0, 1.5: 2.0, 2.5: 2.0, 0.5: 0.0, 0.75: 1.0, 0.25: 0.0, 126.5: 126.0,
+             127.5: 128.0, -3.5: -4.0, 3.25: 3.0}
+    got = mx.bf16_round(np.array(list(cases)) * q)
+    np.testing.assert_array_equal(got, np.array(list(cases.values())) * q)
+    assert mx.bf16_round(np.array([127.5 * q]))[0] == 2.0 ** -126
+    # random magnitudes in [2^-149, 2^-126): fp32 subnormals and small
+    # normals, exact in fp32 and fp64, so torch's cast rounds them once
+    mags = np.exp2(RNG.uniform(-149, -126, 100000)).astype(np.float32)
+    v = mags * RNG.choice([-1.0, 1.0], mags.size).astype(np.float32)
+    v = v[np.abs(v) < np.float32(2.0 ** -126)]
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(mx.bf16_round(v.astype(np.float64)), ref)
+    assert np.any(ref != 0) and np.any(np.abs(ref) < 2.0 ** -126)
