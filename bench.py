@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """MoE-layer forward throughput on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config qwen3_decode]
+    python bench.py [--steps K] [--warmup W] [--config hy3]
 
 One step = one moe_layer_forward call (router logits, gate top-k, routing,
 grouped GEMM1 + SwiGLU, grouped GEMM2, shared expert if any, combine) over
@@ -9,7 +9,10 @@ one batch of synthetic tokens already resident in HBM.  W untimed warm-up
 steps, then exactly K timed steps bracketed by torch.cuda.synchronize().
 The grouped GEMM1 kernel (the largest weight stream) is timed with HIP events
 recorded by the library around its launch in every timed step; its roofline
-fraction is reported against MI355X's 8 TB/s HBM.  The CPU oracle is timed on
+fraction is reported against MI355X's 8 TB/s HBM (decode) or its dense MFMA
+peak (prefill, with the HBM fraction and max(t_flop, t_byte) / t beside it).
+The default workload is the largest one, the Hy3-style layer (T = 4096,
+E = 192, shared expert).  The CPU oracle is timed on
 a bounded sample of the same workload on the host's cores.  Prints one JSON
 line on stdout; progress goes to stderr.
 """
@@ -37,7 +40,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="qwen3_decode")
+    ap.add_argument("--config", default="hy3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the second timing of the layer replayed from a captured HIP graph")
@@ -55,10 +58,26 @@ def parse():
     return ap.parse_args()
 
 
-COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_counters_qwen3_decode_T16_E128.md")
-GEMM1_SOURCES = ("expert_routing_grouped_gate_amd/csrc/ffn_bf16.hip",
-                 "expert_routing_grouped_gate_amd/csrc/common.hpp")
-GEMM1_KERNEL = "ffn_skinny<true"
+# GEMM1 (w13 + SwiGLU) of each layer config: the sources its kernel is built
+# from and the kernel-name prefix rocprofv3 reports.  A counter summary
+# (profiles/hbm_counters_<config>.md) records the hash of those sources; its
+# byte counts are reported as roofline.traffic only while the hash matches.
+_CSRC = "expert_routing_grouped_gate_amd/csrc/"
+GEMM1 = {
+    "bf16_decode": ((_CSRC + "ffn_bf16.hip", _CSRC + "common.hpp"), "ffn_skinny<true"),
+    "bf16_prefill": ((_CSRC + "tiled_bf16.hip", _CSRC + "common.hpp", _CSRC + "mxfmt.hpp"), "ffn_tiled4<true"),
+    "w4a8_decode": ((_CSRC + "mx.hip", _CSRC + "common.hpp", _CSRC + "mxfmt.hpp"), "ffn_mx_stream<true"),
+    "w4a8_prefill": ((_CSRC + "mx_tiled.hip", _CSRC + "common.hpp", _CSRC + "mxfmt.hpp"), "ffn_mx_tiled<true"),
+}
+
+
+def gemm1_family(cfg) -> str:
+    decode = cfg.T * cfg.k <= 16 * cfg.E
+    return ("w4a8_" if cfg.fmt == "w4a8" else "bf16_") + ("decode" if decode else "prefill")
+
+
+def counters_md(config: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_counters_{config}.md")
 
 
 class TimingEvent:
@@ -106,10 +125,10 @@ class TimingEvent:
             TimingEvent._hip.hipEventDestroy(self.cuda_event)
 
 
-def gemm1_source_hash() -> str:
+def gemm1_source_hash(family: str) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in GEMM1_SOURCES:
+    for rel in GEMM1[family][0]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -131,6 +150,7 @@ COUNTER_TITLES = {
                          "MXFP4 weights, MXFP8 activations, Zipf router bias)",
     "qwen3_prefill_w4a8": "Qwen3-style prefill layer with W4A8 experts (T=4096, H=4096, E=128, top-8, I=1536, "
                           "MXFP4 weights, MXFP8 activations)",
+    "hy3": "Hy3-style layer (T=4096, H=4096, E=192, top-8 sigmoid x2.826, I=1536, shared expert I=1536, bf16)",
     "add_rmsnorm": "residual add + RMSNorm before the layer (T=4096, H=4096, fp32 + bf16 outputs, bf16 residual)",
 }
 
@@ -143,8 +163,7 @@ def summarize_counters(config, fetch_csv, write_csv, copy_fetch_csv, copy_write_
     cw = max(v for k, v in _counter_means(copy_write_csv).items() if "copyBuffer" in k)
     kib = 1024 * 1024  # the copy moves 1 GiB = 1,048,576 KiB each way
     sf, sw = kib / cf, kib / cw
-    cfg_arg = "" if config == "qwen3_decode" else f" --config {config}"
-    run = f"python $R/bench.py{cfg_arg} --steps 5 --warmup 2 --no-cpu-baseline --no-graph"
+    run = f"python $R/bench.py --config {config} --steps 5 --warmup 2 --no-cpu-baseline --no-graph"
     lines = [f"# HBM byte counters, {COUNTER_TITLES.get(config, config)}", "",
              "Each counter in its own pass (run from /tmp on one MI355X, repo at $R, output under $OUT):", "", "```",
              f"rocprofv3 --pmc FETCH_SIZE -d $OUT/pmc_FETCH_SIZE_{config} -o run --output-format csv -- {run}",
@@ -158,37 +177,59 @@ def summarize_counters(config, fetch_csv, write_csv, copy_fetch_csv, copy_write_
              "| kernel | FETCH_SIZE KiB | read bytes (scaled) | WRITE_SIZE KiB | written bytes (scaled) |",
              "|---|---|---|---|---|"]
     g1 = None
+    family = None
+    if config in _layer_configs():
+        family = gemm1_family(_layer_configs()[config])
     for k in sorted(fetch, key=lambda k: -fetch[k]):
         if not k.startswith(("void moe::", "moe::")):
             continue
         rb, wb = fetch[k] * sf * 1024, write.get(k, 0.0) * sw * 1024
         lines.append(f"| `{k[:80]}` | {fetch[k]:,.1f} | {rb / 1e9:.4f} GB | {write.get(k, 0.0):,.1f} | {wb / 1e6:.3f} MB |")
-        if GEMM1_KERNEL in k:
+        if family is not None and GEMM1[family][1] in k and g1 is None:
             g1 = (rb, wb)
-    if config == "qwen3_decode":
+    if family is not None:
         lines += ["", "Machine-readable (bench.py reports `roofline.traffic` from these only while the GEMM1 "
                   "sources still hash to the value below):", "",
-                  f"gemm1_source_sha256_16: {gemm1_source_hash()}",
+                  f"gemm1_kernel: {GEMM1[family][1]}",
+                  f"gemm1_source_sha256_16: {gemm1_source_hash(family)}",
                   f"gemm1_read_bytes: {int(g1[0]) if g1 else 0}",
                   f"gemm1_write_bytes: {int(g1[1]) if g1 else 0}"]
     lines.append("")
     print("\n".join(lines))
 
 
-def measured_gemm1_traffic():
-    """HBM bytes per GEMM1 launch from the committed counter summary, or None
-    when it is missing or was taken on different GEMM1 sources."""
+def _layer_configs():
+    from expert_routing_grouped_gate_amd import workloads as W
+    return W.CONFIGS
+
+
+def measured_gemm1_traffic(cfg):
+    """HBM bytes per GEMM1 launch from the committed counter summary of this
+    config, or None when it is missing or was taken on other GEMM1 sources."""
+    family = gemm1_family(cfg)
     try:
         kv = {}
-        for line in open(COUNTERS_MD):
-            if ":" in line and line.split(":")[0].strip() in ("gemm1_source_sha256_16", "gemm1_read_bytes", "gemm1_write_bytes"):
+        for line in open(counters_md(cfg.name)):
+            if ":" in line and line.split(":")[0].strip() in ("gemm1_source_sha256_16", "gemm1_read_bytes",
+                                                              "gemm1_write_bytes"):
                 a, b = line.split(":", 1)
                 kv[a.strip()] = b.strip()
-        if kv.get("gemm1_source_sha256_16") != gemm1_source_hash():
+        if kv.get("gemm1_source_sha256_16") != gemm1_source_hash(family):
             return None
         return int(kv["gemm1_read_bytes"]) + int(kv["gemm1_write_bytes"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def calibrate_copy(mib: int):
@@ -225,7 +266,7 @@ def workload_bytes_flops(cfg, counts):
     g1_bytes = n_touched * w13_e + cfg.T * cfg.H * 2 + act_b
     g1_flops = 2 * R * 2 * cfg.I * cfg.H
     return dict(n_touched=n_touched, layer_bytes=layer_bytes, flops=flops,
-                g1_bytes=int(g1_bytes), g1_flops=g1_flops)
+                g1_bytes=int(g1_bytes), g1_flops=g1_flops, g1_shared=False)
 
 
 def cpu_baseline(cfg, cpu, budget_s):
@@ -261,7 +302,8 @@ def cpu_baseline(cfg, cpu, budget_s):
     cores = max([torch.get_num_threads()] + blas)
     return {"value": done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {done} of {cfg.T} tokens of the same layer, one oracle call per token "
-                      f"(fp64 numpy; routing over all tokens each call), {dt:.1f} s"}
+                      f"(fp64 numpy; routing over all tokens each call), {dt:.1f} s",
+            "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count()}
 
 
 NORM_CONFIGS = {
@@ -378,7 +420,8 @@ def bench_norm(args):
         dt = time.perf_counter() - t1
         blas = [i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
         cpu_b = {"value": round(n * T / dt, 1), "unit": "tokens/s", "cores": max([1] + blas), "kind": "oracle",
-                 "sample": f"{n} oracle calls over all {T} tokens (fp64 numpy), {dt:.1f} s"}
+                 "sample": f"{n} oracle calls over all {T} tokens (fp64 numpy), {dt:.1f} s",
+                 "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count()}
     form = "MXFP8 codes + scales and bf16 residual" if use_mx else "fp32 + bf16 outputs and bf16 residual"
     res = {
         "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -528,16 +571,23 @@ def main():
     layer_tflops = wl["flops"] / (ms * 1e-3) / 1e12
     # the contraction's own dense peak: bf16, or fp8 for the scaled FP8 x FP4 MFMA
     mfma_peak = FP8_PEAK_TFLOPS if cfg.fmt == "w4a8" else BF16_PEAK_TFLOPS
+    traffic = measured_gemm1_traffic(cfg)
+    g1_t_byte = wl["g1_bytes"] / (HBM_PEAK_GBS * 1e9)
+    g1_t_flop = wl["g1_flops"] / (mfma_peak * 1e12)
     if decode:
-        traffic = measured_gemm1_traffic() if cfg.name == "qwen3_decode" else None
         roof = {"bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
     else:
         g1_tf = wl["g1_flops"] / (g1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(g1_tf, 1), "peak": mfma_peak, "unit": "TFLOP/s",
-                "frac": round(g1_tf / mfma_peak, 4), "traffic": None}
-    roof.update({"kernel": "grouped GEMM1 (w13 + SwiGLU)", "kernel_ms": round(g1_ms, 4),
+                "frac": round(g1_tf / mfma_peak, 4), "traffic": traffic,
+                "hbm_gbs": round(g1_gbs, 1), "hbm_frac": round(g1_gbs / HBM_PEAK_GBS, 4)}
+    roof.update({"kernel": f"grouped GEMM1 (w13 + SwiGLU{' + shared expert' if wl['g1_shared'] else ''})",
+                 "kernel_ms": round(g1_ms, 4),
+                 "roof_frac": round(max(g1_t_byte, g1_t_flop) / (g1_ms * 1e-3), 4),
                  "algorithmic_bytes": wl["g1_bytes"], "algorithmic_flops": wl["g1_flops"]})
+    layer_t_byte = wl["layer_bytes"] / (HBM_PEAK_GBS * 1e9)
+    layer_t_flop = wl["flops"] / (mfma_peak * 1e12)
 
     cpu_b = None
     if not args.no_cpu_baseline:
@@ -556,6 +606,8 @@ def main():
                    "experts_touched": wl["n_touched"], "parallelism": "single GPU"},
         "layer": {"hbm_gbs": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / HBM_PEAK_GBS, 4),
                   "tflops": round(layer_tflops, 2), "mfma_frac": round(layer_tflops / mfma_peak, 4),
+                  "roof_frac": round(max(layer_t_byte, layer_t_flop) / (ms * 1e-3), 4),
+                  "roof_bound": "hbm" if layer_t_byte >= layer_t_flop else "mfma",
                   "algorithmic_bytes": wl["layer_bytes"], "flops": wl["flops"]},
         "roofline": roof,
         "cpu_baseline": cpu_b,

@@ -80,6 +80,7 @@ SIGNATURES = {
                              _vp, _vp, _vp, _vp]),
     "moe_combine": (_I, [_vp, _vp, _vp, _vp, _I, _I, _I, _vp, _vp]),
     "moe_layer_workspace_size": (_SZ, [_P(MoeLayerDesc), _I]),
+    "moe_workspace_size": (_SZ, [_P(MoeLayerDesc), _I]),
     "moe_layer_forward": (_I, [_P(MoeLayerDesc), _vp, _I, _vp, _P(MoeLayerBuffers), _vp]),
 }
 

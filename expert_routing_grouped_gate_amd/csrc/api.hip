@@ -424,6 +424,8 @@ size_t moe_layer_workspace_size(const MoeLayerDesc* d, int T) {
   return r > h ? r : h;
 }
 
+size_t moe_workspace_size(const MoeLayerDesc* d, int T) { return moe_layer_workspace_size(d, T); }
+
 int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t* out,
                       const MoeLayerBuffers* b, void* stream) {
   int st;

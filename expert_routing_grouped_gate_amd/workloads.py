@@ -57,6 +57,7 @@ class LayerConfig:
     fmt: str = "bf16"      # "bf16" | "w4a8" (MXFP4 weights, MXFP8 activations)
     family_seed: int = 0   # weights are shared by configs of one model family
     x_seed: int = 0
+    mx_scales: str = "narrow"  # W4A8 block scales: "narrow" (mostly 2^-7) | "wide" (2^-27 .. 2^13)
 
     def with_(self, **kw) -> "LayerConfig":
         return dataclasses.replace(self, **kw)
@@ -86,6 +87,12 @@ CONFIGS = {
     "qwen3_prefill_w4a8": LayerConfig("qwen3_prefill_w4a8", T=4096, H=4096, E=128, k=8, I=1536,
                                       fmt="w4a8", family_seed=1005, x_seed=6),
 }
+
+# Mid-size token counts of the Qwen3-style layer (same weights), around the
+# switch from the weight-streaming GEMMs (at most 16 rows per expert on
+# average: T * k <= 16 * E, i.e. T <= 256 here) to the LDS-tiled ones.
+for _T in (64, 128, 256, 320, 512, 1024):
+    CONFIGS[f"qwen3_T{_T}"] = CONFIGS["qwen3_decode"].with_(name=f"qwen3_T{_T}", T=_T, x_seed=100 + _T)
 
 
 def _seed(*parts: int) -> int:
@@ -160,6 +167,8 @@ def draw_shared_bf16(cfg: LayerConfig) -> Tuple[torch.Tensor, torch.Tensor]:
 _E2M1_MAG_P = (0.078, 0.077, 0.141, 0.125, 0.121, 0.221, 0.142, 0.095)
 _E8M0_CODES = (119, 120, 121)
 _E8M0_P = (0.02, 0.925, 0.055)
+# "wide": every code from 100 to 140 equally likely (scales 2^-27 .. 2^13)
+_E8M0_WIDE = tuple(range(100, 141))
 
 
 def _categorical(p, n: int, g: torch.Generator) -> torch.Tensor:
@@ -169,24 +178,27 @@ def _categorical(p, n: int, g: torch.Generator) -> torch.Tensor:
     return torch.searchsorted(cdf, u, right=True).clamp_(max=len(p) - 1)
 
 
-def _mx_block(rows: int, cols: int, *parts: int) -> Tuple[torch.Tensor, torch.Tensor]:
+def _mx_block(rows: int, cols: int, *parts: int, wide: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """MXFP4 codes [rows, cols/2] (low nibble = even column) and E8M0 scales
-    [rows, cols/32] for a rows x cols weight (cols = reduction dimension)."""
+    [rows, cols/32] for a rows x cols weight (cols = reduction dimension).
+    wide: block scale codes uniform over 100..140 instead of mostly 120."""
     g = _gen(*parts)
     mag = _categorical(_E2M1_MAG_P, rows * cols, g).to(torch.uint8)
     sign = torch.randint(0, 2, (rows * cols,), generator=g, dtype=torch.uint8)
     nib = (mag | (sign << 3)).view(rows, cols)
     codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).contiguous()
-    sidx = _categorical(_E8M0_P, rows * (cols // 32), g)
-    scales = torch.tensor(_E8M0_CODES, dtype=torch.uint8)[sidx].view(rows, cols // 32)
+    table = _E8M0_WIDE if wide else _E8M0_CODES
+    sidx = _categorical((1.0,) * len(table) if wide else _E8M0_P, rows * (cols // 32), g)
+    scales = torch.tensor(table, dtype=torch.uint8)[sidx].view(rows, cols // 32)
     return codes, scales.contiguous()
 
 
 def draw_expert_mx(cfg: LayerConfig, e: int):
     """Expert e's W4A8 weights: (w13_codes [2I, H/2], w13_scales [2I, H/32],
     w2_codes [H, I/2], w2_scales [H, I/32]), all uint8."""
-    c13, s13 = _mx_block(2 * cfg.I, cfg.H, cfg.family_seed, _TAG_MX_W13, e, cfg.I, cfg.H)
-    c2, s2 = _mx_block(cfg.H, cfg.I, cfg.family_seed, _TAG_MX_W2, e, cfg.I, cfg.H)
+    wide = cfg.mx_scales == "wide"
+    c13, s13 = _mx_block(2 * cfg.I, cfg.H, cfg.family_seed, _TAG_MX_W13, e, cfg.I, cfg.H, wide=wide)
+    c2, s2 = _mx_block(cfg.H, cfg.I, cfg.family_seed, _TAG_MX_W2, e, cfg.I, cfg.H, wide=wide)
     return c13, s13, c2, s2
 
 
@@ -196,8 +208,9 @@ def draw_shared_mx(cfg: LayerConfig):
     experts."""
     assert cfg.shared_I > 0
     Is = cfg.shared_I
-    c13, s13 = _mx_block(2 * Is, cfg.H, cfg.family_seed, _TAG_MX_SHARED, 0, Is, cfg.H)
-    c2, s2 = _mx_block(cfg.H, Is, cfg.family_seed, _TAG_MX_SHARED, 1, Is, cfg.H)
+    wide = cfg.mx_scales == "wide"
+    c13, s13 = _mx_block(2 * Is, cfg.H, cfg.family_seed, _TAG_MX_SHARED, 0, Is, cfg.H, wide=wide)
+    c2, s2 = _mx_block(cfg.H, Is, cfg.family_seed, _TAG_MX_SHARED, 1, Is, cfg.H, wide=wide)
     return c13, s13, c2, s2
 
 

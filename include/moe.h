@@ -349,7 +349,13 @@ typedef struct {
   void* ev_ffn_up_end;
 } MoeLayerBuffers;
 
+/* Device scratch moe_layer_forward needs for T tokens (bytes; 0 when none or
+ * for invalid arguments).  moe_workspace_size is the same function under the
+ * name the layer's scratch query carries in the routing operator split
+ * (init_routing / grouped matmul / finalize_routing, [Qwen3] "GMM enablement
+ * and routing optimisation"); either may be called. */
 size_t moe_layer_workspace_size(const MoeLayerDesc* d, int T);
+size_t moe_workspace_size(const MoeLayerDesc* d, int T);
 int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t* out,
                       const MoeLayerBuffers* b, void* stream);
 

@@ -129,13 +129,19 @@ def silu(g):
         return g / (1.0 + np.exp(-g))
 
 
-def expert_ffn(xrows, w13, w2, act: str = "bf16") -> np.ndarray:
+def expert_ffn(xrows, w13, w2, act: str = "bf16", act_exponents=None,
+               stats: Optional[dict] = None) -> np.ndarray:
     """[Qwen3] expert FFN x -> down(SiLU(gate x) * up x) with w13 = gate_proj
     rows followed by up_proj rows (weights in [out, in] layout).
 
     act = "bf16": the SwiGLU output is rounded to bf16 before the down
     projection; act = "mxfp8": it is quantised to MXFP8 along the
-    intermediate dimension and dequantised.  Returns y [m, H] fp64."""
+    intermediate dimension and dequantised ([Hy3] section 5.2: SwiGLU with
+    group quantisation).  act_exponents ([m, I/32], mxfp8 only): block
+    exponents decided elsewhere, used instead of the rule's own (see
+    mx.mxfp8_quantize).  If ``stats`` is given, the exact block maxima of
+    the SwiGLU output are stored in stats["amax"] ([m, I/32]).
+    Returns y [m, H] fp64."""
     xrows = np.asarray(xrows, dtype=F64)
     w13 = np.asarray(w13, dtype=F64)
     w2 = np.asarray(w2, dtype=F64)
@@ -143,10 +149,12 @@ def expert_ffn(xrows, w13, w2, act: str = "bf16") -> np.ndarray:
     g = xrows @ w13[:I].T
     u = xrows @ w13[I:].T
     a = silu(g) * u
+    if stats is not None and act == "mxfp8":
+        stats["amax"] = np.abs(a).reshape(a.shape[0], I // 32, 32).max(-1)
     if act == "bf16":
         a = mx.bf16_round(a)
     elif act == "mxfp8":
-        a = mx.mxfp8_dequant(*mx.mxfp8_quantize(a))
+        a = mx.mxfp8_dequant(*mx.mxfp8_quantize(a, act_exponents))
     else:
         raise ValueError(act)
     return a @ w2.T
@@ -182,7 +190,8 @@ def gate(logits, k: int, mode: str, bias=None, routed_scale: float = 1.0, eps: f
 def layer_forward(x, wr, k: int, mode: str, expert_weights: Callable[[int], tuple],
                   E: int, bias=None, routed_scale: float = 1.0, eps: float = 1e-20,
                   shared_weights: Optional[tuple] = None, fmt: str = "bf16",
-                  logits=None, tokens: Optional[Sequence[int]] = None) -> dict:
+                  logits=None, tokens: Optional[Sequence[int]] = None,
+                  act_exponents=None, shared_act_exponents=None) -> dict:
     """The whole layer: S1 logits, S2 gate, S3/S4 routing, S5/S6 expert FFNs
     over the permuted rows, S7 combine (+ shared expert).
 
@@ -195,6 +204,16 @@ def layer_forward(x, wr, k: int, mode: str, expert_weights: Callable[[int], tupl
     expert FFNs and the combine are evaluated only for those tokens (routing
     is still computed for all tokens); ``out`` then has one row per listed
     token.
+
+    act_exponents ([T*k, I/32], indexed by permuted row) and
+    shared_act_exponents ([T, I_s/32], by token), W4A8 only: the MXFP8 block
+    exponents of the SwiGLU outputs decided by another computation (the
+    GPU's, from its own fp32 values), used instead of the rule's own, like
+    ``logits`` for the selection.  The exact block maxima of the SwiGLU
+    outputs are returned (act_amax [T*k, I/32] by permuted row, NaN for rows
+    not evaluated; shared_act_amax [len(tokens), I_s/32]) so that a caller
+    can check that the exponents it passed differ from the rule's only
+    where the rule's own decision sits at a power of two.
     """
     x = np.asarray(x, dtype=F64)
     T = x.shape[0]
@@ -214,6 +233,7 @@ def layer_forward(x, wr, k: int, mode: str, expert_weights: Callable[[int], tupl
     H = x.shape[1]
     R = T * k
     y = np.zeros((R, H), dtype=F64) if tokens is None else {}
+    act_amax = None
     for e in range(E):
         rows = np.arange(offsets[e], offsets[e + 1])
         if rows.size == 0:
@@ -223,15 +243,25 @@ def layer_forward(x, wr, k: int, mode: str, expert_weights: Callable[[int], tupl
         if not keep.any():
             continue
         w13, w2 = expert_weights(e)
-        ye = expert_ffn(xin[t_of_row[keep]], w13, w2, act)
+        st = {}
+        ex = None if act_exponents is None else np.asarray(act_exponents)[rows[keep]]
+        ye = expert_ffn(xin[t_of_row[keep]], w13, w2, act, ex, st)
+        if "amax" in st:
+            if act_amax is None:
+                act_amax = np.full((R, st["amax"].shape[1]), np.nan)
+            act_amax[rows[keep]] = st["amax"]
         if tokens is None:
             y[rows[keep]] = ye
         else:
             for r, v in zip(rows[keep], ye):
                 y[int(r)] = v
     shared = None
+    shared_amax = None
     if shared_weights is not None:
-        shared = expert_ffn(xin[toks], shared_weights[0], shared_weights[1], act)
+        st = {}
+        ex = None if shared_act_exponents is None else np.asarray(shared_act_exponents)[toks]
+        shared = expert_ffn(xin[toks], shared_weights[0], shared_weights[1], act, ex, st)
+        shared_amax = st.get("amax")
     if tokens is None:
         out = combine(y, pair_pos, w, shared)
     else:
@@ -240,4 +270,5 @@ def layer_forward(x, wr, k: int, mode: str, expert_weights: Callable[[int], tupl
         out = combine(yrows, np.arange(pos.size), w[toks], shared)
     return dict(logits=L_ref, ids=ids, w=w, counts=counts, offsets=offsets,
                 sorted_pair=sorted_pair, pair_pos=pair_pos, out=out,
-                x_used=xin if fmt == "w4a8" else None)
+                x_used=xin if fmt == "w4a8" else None,
+                act_amax=act_amax, shared_act_amax=shared_amax)

@@ -132,18 +132,26 @@ def mx_block_exponent(amax, emax_elem: int) -> np.ndarray:
     return np.clip(e, -127, 127).astype(np.int64)
 
 
-def mxfp8_quantize(x) -> tuple:
+def mxfp8_quantize(x, exponents=None) -> tuple:
     """Dynamic MXFP8 quantisation along the last axis (blocks of 32).
 
     Returns (codes uint8 [..., K], scales uint8 [..., K/32]) where
     scale code = shared exponent + 127 and code = E4M3_RNE_sat(x / 2^exp).
+    ``exponents`` ([..., K/32] ints), when given, replaces the shared
+    exponents the rule would take from the block maxima: the elements are
+    then rounded at those exponents (used where another computation decided
+    a block's exponent from its own, rounded values of the same block).
     """
     x = np.asarray(x, dtype=F64)
     K = x.shape[-1]
     assert K % 32 == 0
     blocks = x.reshape(x.shape[:-1] + (K // 32, 32))
-    amax = np.abs(blocks).max(axis=-1)
-    e = mx_block_exponent(amax, 8)
+    if exponents is None:
+        amax = np.abs(blocks).max(axis=-1)
+        e = mx_block_exponent(amax, 8)
+    else:
+        e = np.asarray(exponents, dtype=np.int64)
+        assert e.shape == blocks.shape[:-1] and np.all((e >= -127) & (e <= 127))
     q = blocks / np.exp2(e.astype(F64))[..., None]
     codes = e4m3_encode_rne(q).reshape(x.shape)
     return codes, (e + 127).astype(np.uint8)

@@ -60,12 +60,12 @@ class Layer:
                                      self.cfg.shared_I))
         return (c["shared_w13"].to(torch.float64).numpy(), c["shared_w2"].to(torch.float64).numpy())
 
-    def oracle(self, logits=None, tokens=None):
+    def oracle(self, logits=None, tokens=None, **kw):
         cfg = self.cfg
         return moe.layer_forward(self.x64(), self.wr(), cfg.k, cfg.gate, self.expert, cfg.E,
                                  bias=self.bias(), routed_scale=cfg.routed_scale, eps=cfg.eps,
                                  shared_weights=self.shared(), fmt=cfg.fmt, logits=logits,
-                                 tokens=tokens)
+                                 tokens=tokens, **kw)
 
 
 _CACHE = {}
@@ -114,3 +114,64 @@ def assert_close_bf16(gpu, ref, atol, rtol, what):
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside |d| <= {atol} + {rtol}|ref|; "
                              f"first at {idx.tolist()}: gpu {g[tuple(idx[0])]} ref {r[tuple(idx[0])]}; "
                              f"max err {err.max()}")
+
+
+def check_ids_on_oracle_logits(cfg: W.LayerConfig, L_ref, bias, ids_gpu, tol: float = 1e-4):
+    """The selection against the oracle's OWN fp64-derived logits (not the
+    GPU's): the GPU logits are within `tol` of L_ref, so a key moves by at
+    most tol (softmax: key = fl32(L + b), plus an fp32 rounding) or tol / 4
+    (sigmoid: the slope of the sigmoid is at most 1/4).  Every token whose
+    k-th and (k+1)-th largest keys (from L_ref) are further apart than twice
+    that must select the same experts; a token whose top-(k+1) keys are all
+    that far apart must list them in the same order.  Returns the number of
+    tokens inside the tie band (reported, and required to be a small
+    minority so that the check has teeth)."""
+    k, E = cfg.k, cfg.E
+    ids_ref, _ = moe.gate(L_ref, k, cfg.gate, bias, cfg.routed_scale, cfg.eps)
+    L32 = np.asarray(L_ref, dtype=np.float32)
+    if cfg.gate == "softmax":
+        key = (L32 if bias is None else L32 + np.asarray(bias, np.float32)[None]).astype(np.float64)
+        thr = 2 * (tol + 2.0 ** -22 * np.abs(key).max())
+    else:
+        s = 1.0 / (1.0 + np.exp(-L32.astype(np.float64)))
+        key = s if bias is None else s + np.asarray(bias, np.float32).astype(np.float64)[None]
+        thr = 2 * (tol / 4) + 1e-12
+    ks = -np.sort(-key, axis=1)
+    m = min(k + 1, E)
+    gaps = ks[:, :m - 1] - ks[:, 1:m]                       # consecutive gaps among the top k+1
+    bound_gap = gaps[:, k - 1] if k < E else np.full(key.shape[0], np.inf)
+    ids_gpu = np.asarray(ids_gpu)
+    sure_set = bound_gap > thr
+    set_ok = np.array([set(a) == set(b) for a, b in zip(ids_gpu[sure_set], ids_ref[sure_set])])
+    assert set_ok.all(), f"{cfg.name}: selection differs from the oracle's own logits outside the tie band"
+    sure_order = np.all(gaps > thr, axis=1) if m > 1 else np.ones(key.shape[0], bool)
+    sure_order &= sure_set
+    assert np.array_equal(ids_gpu[sure_order], ids_ref[sure_order]), f"{cfg.name}: slot order differs"
+    band = int((~sure_set).sum())
+    log(f"[{cfg.name}] selection on the oracle's own logits: {band} of {key.shape[0]} tokens in the "
+        f"tie band (gap <= {thr:.2e}), {int(sure_order.sum())} with a fixed slot order")
+    assert band <= max(2, key.shape[0] // 20), f"{cfg.name}: tie band too wide to check ({band})"
+    return band
+
+
+def expert_rows_to_check(offsets, BM: int = 128, n_extra: int = 1, seed: int = 0):
+    """Experts whose rows a full-size per-expert check takes: the one with
+    the most rows (most m-tiles), the one with the fewest non-zero rows, the
+    one whose last m-tile is the most ragged (fewest rows in its last
+    BM-row tile), the first and last touched expert ids (the ends of the
+    device scheduler's per-lane group ranges), plus a seeded random one."""
+    off = np.asarray(offsets)
+    rows = np.diff(off)
+    touched = np.nonzero(rows)[0]
+    pick = [int(touched[np.argmax(rows[touched])]), int(touched[np.argmin(rows[touched])])]
+    tail = rows[touched] % BM
+    tail = np.where(tail == 0, BM, tail)
+    pick.append(int(touched[np.argmin(tail)]))
+    pick += [int(touched[0]), int(touched[-1])]
+    rng = np.random.default_rng(seed)
+    pick += [int(e) for e in rng.choice(touched, size=min(n_extra, touched.size), replace=False)]
+    out = []
+    for e in pick:
+        if e not in out:
+            out.append(e)
+    return out

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("moe_gate_topk", "moe_route", "moe_grouped_ffn", "moe_combine",
                  "moe_layer_forward", "moe_router_logits", "moe_mx_quantize", "moe_add_rmsnorm",
-                 "moe_status_string", "moe_layer_workspace_size"):
+                 "moe_status_string", "moe_layer_workspace_size", "moe_workspace_size"):
         assert want in names
     assert set(names) == set(B.SIGNATURES), "binding and header disagree"
 
@@ -194,6 +194,9 @@ def test_layer_forward_checks(lib):
     # 16 tokens: the router's partial sums (1 slice x 16 x 8 fp32)
     assert lib.moe_layer_workspace_size(ctypes.byref(d), 16) == 16 * 8 * 4
     assert lib.moe_layer_workspace_size(ctypes.byref(d), 100) == 8 * 100 * 8 * 4  # split-K router
+    for T in (0, 1, 16, 100, 4096):      # the survey's name for the same query
+        assert lib.moe_workspace_size(ctypes.byref(d), T) == lib.moe_layer_workspace_size(ctypes.byref(d), T)
+    assert lib.moe_workspace_size(None, 16) == 0
 
 
 def test_mx_pack_checks_and_sizes(lib):

@@ -64,3 +64,24 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_gemm1_traffic_is_keyed_to_the_config_and_its_sources(tmp_path, monkeypatch):
+    assert bench.gemm1_family(W.CONFIGS["hy3"]) == "bf16_prefill"
+    assert bench.gemm1_family(W.CONFIGS["qwen3_decode"]) == "bf16_decode"
+    assert bench.gemm1_family(W.CONFIGS["qwen3_decode_w4a8"]) == "w4a8_decode"
+    assert bench.gemm1_family(W.CONFIGS["qwen3_prefill_w4a8"]) == "w4a8_prefill"
+    cfg = W.CONFIGS["hy3"]
+    md = tmp_path / "hbm_counters_hy3.md"
+    monkeypatch.setattr(bench, "counters_md", lambda name: str(tmp_path / f"hbm_counters_{name}.md"))
+    assert bench.measured_gemm1_traffic(cfg) is None                     # no summary
+    h = bench.gemm1_source_hash("bf16_prefill")
+    md.write_text(f"gemm1_source_sha256_16: {h}\ngemm1_read_bytes: 1000\ngemm1_write_bytes: 24\n")
+    assert bench.measured_gemm1_traffic(cfg) == 1024
+    md.write_text("gemm1_source_sha256_16: 0000000000000000\ngemm1_read_bytes: 1000\ngemm1_write_bytes: 24\n")
+    assert bench.measured_gemm1_traffic(cfg) is None                     # taken on other sources
+    assert h != bench.gemm1_source_hash("bf16_decode")
+
+
+def test_host_cpu_model_is_named():
+    assert isinstance(bench.host_cpu_model(), str) and bench.host_cpu_model()

@@ -183,6 +183,85 @@ def test_norm_feeds_the_gate_in_fp32():
 
 # ------------------------- S7 fused with the next layer's add + RMSNorm ----
 
+def _norm_bars(out, z, y, what):
+    """The norm's bars (module docstring) for every output of a call against
+    the oracle's z and y of the same combined rows."""
+    np.testing.assert_array_equal(out["residual"].double().cpu().numpy(), mx.bf16_round(z))
+    yf = out["f32"].double().cpu().numpy()
+    err = np.abs(yf - y)
+    assert np.all(err <= RTOL_F32 * np.abs(y)), f"{what}: f32 max rel err {np.max(err / np.maximum(np.abs(y), 1e-30))}"
+    yb = out["bf16"].double().cpu().numpy()
+    np.testing.assert_array_equal(yb, mx.bf16_round(yf))
+    assert np.all(np.abs(yb - mx.bf16_round(y)) <= _bf16_step(y)), what
+    codes, scales = mx.mxfp8_quantize(yf)
+    np.testing.assert_array_equal(out["mx"][0].cpu().numpy(), codes)
+    np.testing.assert_array_equal(out["mx"][1].cpu().numpy(), scales)
+
+
+def _combine_bound(y64, pp_np, w_np, sh64, ref_out):
+    """Largest distance between the kernel's combined row (fp32 slot sums
+    rounded to bf16) and the oracle's (fp64 sums rounded to bf16): the fp32
+    sum of k (+1 shared) products is within (k + 2) 2^-24 of the sum of
+    their magnitudes, and the two roundings to bf16 add at most one bf16
+    step of the larger value."""
+    T, k = w_np.shape
+    mag = np.zeros_like(ref_out)
+    pos = pp_np.reshape(T, k)
+    for j in range(k):
+        mag += np.abs(w_np[:, j:j + 1].astype(np.float64)) * np.abs(y64[pos[:, j]])
+    if sh64 is not None:
+        mag += np.abs(sh64)
+    e = (k + 2) * 2.0 ** -24 * mag
+    return e + _bf16_step(np.abs(ref_out) + e) + 1e-30
+
+
+def _fused_vs_oracle(fused, y, pp, w, shared, weight, eps, res):
+    """Every output of moe_combine_add_rmsnorm against the oracle.
+
+    (1) oracle/norm.add_rmsnorm of the call's own combined rows (its `out`
+    output): the norm's bars, bit for bit where they are exact.
+    (2) The oracle's whole chain: oracle/moe.combine of the same expert
+    rows, then oracle/norm.add_rmsnorm.  The combined rows may differ by
+    the bound of _combine_bound (fp32 against fp64 slot sums, then bf16
+    roundings), and such a difference dz_i
+    carries through the norm: y_i changes by |w_i| r dz_i directly and every
+    y_j by |y_j| |dr / r| through the row's root, |dr / r| <= |d mean(z^2)| /
+    (2 (mean(z^2) + eps)).  The f32 output must lie within that plus the
+    norm's own 1e-5; bf16 and the residual within it plus one bf16 step; the
+    MXFP8 output (dequantised) within it plus the format's rounding bound."""
+    from oracle import moe
+    y64, pp_np, w_np = y.double().cpu().numpy(), pp.cpu().numpy(), w.cpu().numpy()
+    sh64 = None if shared is None else shared.double().cpu().numpy()
+    res64 = None if res is None else res.double().cpu().numpy()
+    g64 = weight.double().cpu().numpy()
+    got_out = fused["out"].double().cpu().numpy()
+    ref_out = moe.combine(y64, pp_np, w_np, sh64)
+    dz = np.abs(got_out - ref_out)
+    assert np.all(dz <= _combine_bound(y64, pp_np, w_np, sh64, ref_out)), "combined rows"
+    z1, y1 = norm.add_rmsnorm(got_out, res64, g64, eps)            # (1)
+    _norm_bars(fused, z1, y1, "fused vs oracle norm of its own rows")
+    z2, y2 = norm.add_rmsnorm(ref_out, res64, g64, eps)            # (2)
+    H = z2.shape[1]
+    ms2 = np.sum(z2 * z2, axis=1, keepdims=True) / H
+    r2 = 1.0 / np.sqrt(ms2 + eps)
+    dms = np.abs(np.sum(z1 * z1 - z2 * z2, axis=1, keepdims=True)) / H
+    drel = 0.5 * dms / (ms2 + eps) * 1.01
+    prop = np.abs(g64)[None] * r2 * dz * 1.01 + np.abs(y2) * drel
+    bound = RTOL_F32 * np.abs(y2) + prop + 1e-30
+    yf = fused["f32"].double().cpu().numpy()
+    assert np.all(np.abs(yf - y2) <= bound), "f32 vs the oracle's chain"
+    yb = fused["bf16"].double().cpu().numpy()
+    assert np.all(np.abs(yb - y2) <= bound + _bf16_step(y2)), "bf16 vs the oracle's chain"
+    rz = fused["residual"].double().cpu().numpy()
+    assert np.all(np.abs(rz - z2) <= dz + _bf16_step(z2) + 1e-30), "residual vs the oracle's chain"
+    scale = np.repeat(mx.e8m0_decode(fused["mx"][1].cpu().numpy()), 32, axis=-1)
+    deq = mx.mxfp8_dequant(fused["mx"][0].cpu().numpy(), fused["mx"][1].cpu().numpy())
+    q_err = np.where(np.abs(yf) > 448 * scale, np.abs(yf) - 448 * scale,
+                     np.maximum(2.0 ** -4 * np.abs(yf), 2.0 ** -10 * scale))
+    assert np.all(np.abs(deq - y2) <= bound + q_err * (1 + 1e-12)), "MXFP8 vs the oracle's chain"
+    rows_same = np.mean(np.all(dz == 0, axis=1))
+    print(f"fused vs oracle chain: {rows_same:.3f} of rows combine identically", flush=True)
+
 def _separate(y, pp, w, shared, weight, eps, res):
     out = B.combine(y, pp, w, shared)
     n = B.add_rmsnorm(out, weight, eps, res, mx=True)
@@ -218,7 +297,10 @@ def test_combine_add_rmsnorm_equals_separate_calls_on_a_layer(with_shared, with_
     ref = moe.combine(b["y"].double().cpu().numpy(), b["pair_pos"].cpu().numpy(),
                       b["topk_w"].cpu().numpy(), None if shared is None else shared.double().cpu().numpy())
     got = out.double().cpu().numpy()
-    assert np.all(np.abs(got - ref) <= _bf16_step(ref) + 1e-30)   # fp32 vs fp64 sums: one bf16 step
+    assert np.all(np.abs(got - ref) <= _combine_bound(b["y"].double().cpu().numpy(), b["pair_pos"].cpu().numpy(),
+                                                      b["topk_w"].cpu().numpy(),
+                                                      None if shared is None else shared.double().cpu().numpy(), ref))
+    _fused_vs_oracle(fused, b["y"], b["pair_pos"], b["topk_w"], shared, weight, 1e-6, res)
 
 
 @pytest.mark.parametrize("T,k,H", [(4096, 8, 4096), (16, 8, 4096), (3, 32, 256), (7, 1, 16384)])
@@ -235,3 +317,4 @@ def test_combine_add_rmsnorm_equals_separate_calls(T, k, H):
     for key in ("f32", "bf16", "residual"):
         assert torch.equal(fused[key], n[key]), key
     assert torch.equal(fused["mx"][0], n["mx"][0]) and torch.equal(fused["mx"][1], n["mx"][1])
+    _fused_vs_oracle(fused, y, pp, w, None, g, 1e-6, r)

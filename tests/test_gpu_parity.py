@@ -11,7 +11,8 @@ import torch
 from expert_routing_grouped_gate_amd import binding as B
 from expert_routing_grouped_gate_amd import workloads as W
 from oracle import moe, mx
-from tests.layer_fixtures import assert_close_bf16, get_layer, log
+from tests.layer_fixtures import (assert_close_bf16, check_ids_on_oracle_logits, expert_rows_to_check,
+                                  get_layer, log)
 
 pytestmark = pytest.mark.gpu
 
@@ -226,6 +227,7 @@ def _layer_check(cfg, tokens=None):
     res = L.oracle(logits=gl, tokens=tokens)
     np.testing.assert_allclose(gl, res["logits"], atol=1e-4, rtol=0)
     assert np.array_equal(to_np(b["topk_ids"]), res["ids"])
+    check_ids_on_oracle_logits(cfg, res["logits"], L.bias(), to_np(b["topk_ids"]))
     np.testing.assert_allclose(to_np(b["topk_w"]), res["w"], rtol=1e-6, atol=1e-7)
     for key in ("counts", "offsets", "sorted_pair", "pair_pos"):
         assert np.array_equal(to_np(b[key]), res[key]), key
@@ -316,6 +318,64 @@ FULL = [("qwen3_decode", None), ("qwen3_prefill", [0, 1, 2, 777, 2048, 4094, 409
 @pytest.mark.parametrize("name,tokens", FULL, ids=[f[0] for f in FULL])
 def test_layer_full_size(name, tokens):
     _layer_check(CFG[name], tokens)
+
+
+def _expert_rows_check(L, b, experts):
+    """act and y of whole experts of a layer call, element by element: act
+    against the oracle's bf16(SiLU(x Wg^T) * (x Wu^T)) of the expert's
+    gathered tokens, y against the GPU's own act times W2^T (isolating
+    GEMM2)."""
+    cfg = L.cfg
+    sp, off = to_np(b["sorted_pair"]), to_np(b["offsets"])
+    x64 = L.x64()
+    I = cfg.I
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        w13, w2 = L.expert(e)
+        xr = x64[sp[r0:r1] // cfg.k]
+        a = mx.bf16_round(moe.silu(xr @ w13[:I].T) * (xr @ w13[I:].T))
+        ag = bf16_np(b["act"][r0:r1])
+        assert_close_bf16(ag, a, ATOL, RTOL, f"{cfg.name} act expert {e} ({r1 - r0} rows)")
+        assert_close_bf16(bf16_np(b["y"][r0:r1]), ag @ w2.T, ATOL, RTOL, f"{cfg.name} y expert {e}")
+    log(f"[{cfg.name}] expert rows checked: " + ", ".join(f"{e} ({int(off[e + 1] - off[e])} rows)" for e in experts))
+
+
+@pytest.mark.parametrize("name", ["qwen3_prefill", "hy3"])
+def test_full_size_expert_rows(name):
+    """At the full prefill shapes, whole experts' GEMM1 and GEMM2 rows: the
+    expert with the most rows (most m-tiles), the fewest, the most ragged
+    last m-tile, the first and last touched ids and a random one; for Hy3
+    also the shared expert's rows on a token sample that spans its
+    128-row tiles."""
+    L = get_layer(CFG[name])
+    layer = L.layer()
+    layer.forward(L.dev["x"])
+    torch.cuda.synchronize()
+    b = layer.buf
+    experts = expert_rows_to_check(to_np(b["offsets"]), seed=len(name))
+    assert len(experts) >= 4
+    _expert_rows_check(L, b, experts)
+    if L.cfg.shared_I:
+        toks = np.unique(np.concatenate([np.arange(0, 4096, 61), [127, 128, 255, 256, 4094, 4095]]))
+        w13, w2 = L.shared()
+        Is = L.cfg.shared_I
+        xr = L.x64()[toks]
+        a = mx.bf16_round(moe.silu(xr @ w13[:Is].T) * (xr @ w13[Is:].T))
+        ag = bf16_np(b["shared_act"])[toks]
+        assert_close_bf16(ag, a, ATOL, RTOL, f"{name} shared act")
+        assert_close_bf16(bf16_np(b["shared_y"])[toks], ag @ w2.T, ATOL, RTOL, f"{name} shared y")
+
+
+# mid-size token counts around the switch from the weight-streaming GEMMs
+# (T * k <= 16 * E: T <= 256 at E = 128, k = 8) to the LDS-tiled ones, at the
+# full hidden and expert sizes; values on every token
+MID = {"qwen3_T256": CFG["qwen3_T256"],
+       "qwen3_T264": CFG["qwen3_T256"].with_(name="qwen3_T264", T=264, x_seed=364)}
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_layer_mid_size(name):
+    _layer_check(MID[name])
 
 
 # ------------------------------------------------------- degenerate cases --

@@ -434,3 +434,24 @@ def test_bf16_round_subnormals():
     ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(mx.bf16_round(v.astype(np.float64)), ref)
     assert np.any(ref != 0) and np.any(np.abs(ref) < 2.0 ** -126)
+
+
+def test_mxfp8_quantize_at_given_exponents():
+    """Quantising at exponents decided elsewhere: the rule's own exponents
+    reproduce the default; a block whose exact maximum 3.99999557 sits just
+    below 4 takes exponent floor(log2) - 8 = -7, so that element scales to
+    511.9994 and saturates to 448 (3.5), while at exponent -6 it rounds to
+    256 (4.0) (hand-worked)."""
+    x = RNG.standard_normal((3, 64))
+    c0, s0 = mx.mxfp8_quantize(x)
+    c1, s1 = mx.mxfp8_quantize(x, s0.astype(np.int64) - 127)
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+    b = np.zeros((1, 32))
+    b[0, 0] = 3.99999557
+    b[0, 1] = 1.0
+    c, s = mx.mxfp8_quantize(b)
+    assert s.tolist() == [[120]]
+    assert mx.mxfp8_dequant(c, s)[0, :2].tolist() == [3.5, 1.0]
+    c, s = mx.mxfp8_quantize(b, np.array([[-6]]))
+    assert s.tolist() == [[121]]
+    assert mx.mxfp8_dequant(c, s)[0, :2].tolist() == [4.0, 1.0]

@@ -46,3 +46,20 @@ def test_mx_shared_expert_drawn_with_layer():
     assert t["shared_w2"].shape == (256, 64) and t["shared_w2_scales"].shape == (256, 4)
     c13, _, _, _ = W.draw_expert_mx(c, 0)
     assert not torch.equal(t["shared_w13"], c13)   # its own stream, not expert 0's
+
+
+def test_mx_wide_scales_span_the_range():
+    narrow = W.CONFIGS["qwen3_decode_w4a8"].with_(H=256, I=128)
+    wide = narrow.with_(mx_scales="wide")
+    c13n, s13n, _, _ = W.draw_expert_mx(narrow, 0)
+    c13w, s13w, _, s2w = W.draw_expert_mx(wide, 0)
+    assert torch.equal(c13n, c13w)                 # same element codes, other scales
+    u = set(torch.unique(torch.cat([s13w.ravel(), s2w.ravel()])).tolist())
+    assert min(u) == 100 and max(u) == 140 and len(u) == 41
+
+
+def test_mid_size_configs_share_the_decode_weights():
+    for T in (64, 128, 256, 320, 512, 1024):
+        c = W.CONFIGS[f"qwen3_T{T}"]
+        assert c.T == T and c.family_seed == W.CONFIGS["qwen3_decode"].family_seed
+        assert (c.H, c.E, c.k, c.I) == (4096, 128, 8, 1536)
