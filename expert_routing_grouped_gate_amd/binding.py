@@ -82,7 +82,9 @@ SIGNATURES = {
     "moe_layer_workspace_size": (_SZ, [_P(MoeLayerDesc), _I]),
     "moe_workspace_size": (_SZ, [_P(MoeLayerDesc), _I]),
     "moe_layer_forward": (_I, [_P(MoeLayerDesc), _vp, _I, _vp, _P(MoeLayerBuffers), _vp]),
+    "moe_layer_forward_noalloc": (_I, [_P(MoeLayerDesc), _vp, _I, _vp, _P(MoeLayerBuffers), _vp]),
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -444,5 +446,19 @@ class MoeLayer:
         if out is None:
             out = torch.empty((T, self.w.H), dtype=torch.bfloat16, device=x.device)
         _check("moe_layer_forward", load().moe_layer_forward(
+            _c.byref(self.desc), _ptr(x), T, _ptr(out), _c.byref(self.cbuf), _stream()))
+        return out
+
+    def forward_noalloc(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """One moe_layer_forward_noalloc call: the same layer with the
+        library's static scratch in place of the workspace buffer."""
+        _dev(x)
+        assert x.dtype == torch.bfloat16
+        T = x.shape[0]
+        if self._T != T:
+            self.alloc(T, x.device)
+        if out is None:
+            out = torch.empty((T, self.w.H), dtype=torch.bfloat16, device=x.device)
+        _check("moe_layer_forward_noalloc", load().moe_layer_forward_noalloc(
             _c.byref(self.desc), _ptr(x), T, _ptr(out), _c.byref(self.cbuf), _stream()))
         return out

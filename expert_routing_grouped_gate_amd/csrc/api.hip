@@ -41,9 +41,33 @@ int resident_grid(const void* kernel, int block, long long max_tiles) {
 
 }  // namespace moe
 
+// The scratch of moe_layer_forward_noalloc: one copy per GPU, in the device
+// code object's zero-initialised data (no file space), loaded with the
+// library.  Host code never uses this name as an address (on the host it is
+// only a stand-in): scratch_device_ptr() asks the runtime for the address on
+// the current GPU once and keeps it per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using moe::GroupedGemm;
+
+// Device address of `scratch` on the current GPU, or nullptr when the runtime
+// cannot give it.  Looked up once per device (hipGetSymbolAddress with that
+// device current) and kept.
+void* scratch_device_ptr() {
+  static std::mutex mu;
+  static void* ptrs[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -134,6 +158,7 @@ const char* moe_status_string(int code) {
     case MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case MOE_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_SCRATCH: return "the call needs more than the library's static scratch";
     default: return "unknown status";
   }
 }
@@ -491,6 +516,24 @@ int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t*
     return st;
   return moe_combine(b->y, b->pair_pos, b->topk_w, shared ? b->shared_y : nullptr, T, k, d->H,
                      out, stream);
+}
+
+int moe_layer_forward_noalloc(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t* out,
+                              const MoeLayerBuffers* b, void* stream) {
+  if (d == nullptr || b == nullptr) return MOE_ERR_NULL;
+  if (T < 0) return MOE_ERR_SHAPE;
+  if (moe_layer_workspace_size(d, T) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  MoeLayerBuffers s = *b;
+  s.workspace = nullptr;
+  s.workspace_bytes = 0;
+  if (T > 0) {
+    // moe_layer_forward validates everything else before it enqueues
+    void* p = scratch_device_ptr();
+    if (p == nullptr) return MOE_ERR_LAUNCH;
+    s.workspace = p;
+    s.workspace_bytes = MOE_NOALLOC_SCRATCH_BYTES;
+  }
+  return moe_layer_forward(d, x, T, out, &s, stream);
 }
 
 }  // extern "C"

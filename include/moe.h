@@ -46,7 +46,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = -3, /* outside the limits above, or unknown mode/format */
   MOE_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
   MOE_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch */
-  MOE_ERR_WORKSPACE = -6    /* workspace missing or smaller than required */
+  MOE_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required */
+  MOE_ERR_SCRATCH = -7      /* the call needs more than the library's static scratch */
 } moe_status;
 
 /* Gating modes (S2). */
@@ -358,6 +359,30 @@ size_t moe_layer_workspace_size(const MoeLayerDesc* d, int T);
 size_t moe_workspace_size(const MoeLayerDesc* d, int T);
 int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t* out,
                       const MoeLayerBuffers* b, void* stream);
+
+/* ------------------------------------------- whole layer, no allocation -----
+ * moe_layer_forward for callers that cannot allocate device memory or hand
+ * the library a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, kernels and
+ * results as moe_layer_forward, except that b->workspace and
+ * b->workspace_bytes are ignored: the router's partial sums and the routing
+ * histograms live in one static device array of the library,
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the library's first
+ * use on that GPU until the process ends.  The call allocates nothing.
+ *   Limit: moe_layer_workspace_size(d, T) <= MOE_NOALLOC_SCRATCH_BYTES (the
+ *   router part never exceeds 64 MiB; the routing part does only beyond
+ *   about 60 million routed pairs at E = 256), else MOE_ERR_SCRATCH and
+ *   nothing is enqueued.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents (every byte a call reads from it, that call wrote
+ *   first, so nothing needs to start at zero).  Calls that overlap on one
+ *   GPU (different streams or host threads, or a second call enqueued
+ *   before the first finished on another stream) RACE on it: order them on
+ *   one stream.  MOE_ERR_LAUNCH if the array's device address cannot be
+ *   obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_forward_noalloc(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t* out,
+                              const MoeLayerBuffers* b, void* stream);
 
 #ifdef __cplusplus
 }

@@ -12,7 +12,7 @@ from expert_routing_grouped_gate_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, LAUNCH, WS = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, UNSUP, ALIGN, LAUNCH, WS, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 
 
 def declared_functions():
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, LAUNCH, WS):
+    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, LAUNCH, WS, SCRATCH):
         assert B.status_string(code)
     assert B.status_string(12345) == "unknown status"
 
@@ -218,3 +218,24 @@ def test_w4a8_matrix_size_limit(lib):
     # one expert's E2M1 matrix must be addressable with 32-bit offsets
     big = B.MoeFfnWeights(1 << 16, 1 << 15, 8, B.FMT_W4A8, FAKE, FAKE, FAKE, FAKE, 0, None, None, None, None)
     assert lib.moe_grouped_ffn_up(ctypes.byref(big), FAKE, FAKE, 4, 2, FAKE, FAKE, FAKE, FAKE, None) == UNSUP
+
+
+def test_layer_forward_noalloc_host_checks(lib):
+    """The no-allocation layer call rejects, before anything else, a call
+    whose workspace would exceed the static scratch (here the routing
+    histograms of 2^30 pairs over 256 experts, ~1 GB); argument errors are
+    those of moe_layer_forward; nothing reaches the device."""
+    w = B.MoeFfnWeights(256, 128, 256, B.FMT_BF16, FAKE, None, FAKE, None, 0, None, None, None, None)
+    d = B.MoeLayerDesc(256, 256, 8, 0, 1.0, 1e-20, FAKE, None, w)
+    b = B.MoeLayerBuffers()
+    f = lib.moe_layer_forward_noalloc
+    T = 1 << 27
+    assert lib.moe_layer_workspace_size(ctypes.byref(d), T) > B.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(d), FAKE, T, FAKE, ctypes.byref(b), None) == SCRATCH
+    assert f(None, FAKE, 4, FAKE, ctypes.byref(b), None) == NULL
+    assert f(ctypes.byref(d), FAKE, 4, FAKE, None, None) == NULL
+    assert f(ctypes.byref(d), FAKE, -1, FAKE, ctypes.byref(b), None) == SHAPE
+    assert f(ctypes.byref(d), FAKE, 0, FAKE, ctypes.byref(b), None) == OK    # nothing to do
+    # the largest layer shapes fit: router partials of 4096 tokens x 256 experts
+    assert lib.moe_layer_workspace_size(ctypes.byref(d), 4096) <= B.NOALLOC_SCRATCH_BYTES
+    assert "static scratch" in B.status_string(SCRATCH)
