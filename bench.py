@@ -265,8 +265,16 @@ def workload_bytes_flops(cfg, counts):
     act_b = R * cfg.I * (1 + 1 / 32 if cfg.fmt == "w4a8" else 2)
     g1_bytes = n_touched * w13_e + cfg.T * cfg.H * 2 + act_b
     g1_flops = 2 * R * 2 * cfg.I * cfg.H
+    # bf16 with shared_I == I and many rows per expert: the library runs the
+    # shared expert as one more group of the GEMM1 launch (its w13, its
+    # activations written, its flops)
+    g1_shared = (cfg.fmt == "bf16" and cfg.shared_I > 0 and cfg.shared_I == cfg.I
+                 and cfg.T * cfg.k > 16 * cfg.E)
+    if g1_shared:
+        g1_bytes += 2 * cfg.shared_I * cfg.H * 2 + cfg.T * cfg.shared_I * 2
+        g1_flops += 2 * cfg.T * 2 * cfg.shared_I * cfg.H
     return dict(n_touched=n_touched, layer_bytes=layer_bytes, flops=flops,
-                g1_bytes=int(g1_bytes), g1_flops=g1_flops, g1_shared=False)
+                g1_bytes=int(g1_bytes), g1_flops=g1_flops, g1_shared=g1_shared)
 
 
 def cpu_baseline(cfg, cpu, budget_s):

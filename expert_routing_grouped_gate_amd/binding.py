@@ -376,6 +376,25 @@ def shared_ffn(w: ExpertWeights, x, x_scales=None, shared_act=None, shared_act_s
     return shared_act, shared_act_scales, shared_y
 
 
+def grouped_ffn(w: ExpertWeights, x, x_scales, k: int, sorted_pair, offsets, with_shared: bool = True):
+    """moe_grouped_ffn: GEMM1 + SwiGLU, GEMM2 (and the shared expert when the
+    weights have one and with_shared).  Returns (act, act_scales, y,
+    shared_act, shared_act_scales, shared_y)."""
+    T = x.shape[0]
+    act, act_scales = _act_tensors(T * k, w.I, w.fmt, x.device)
+    y = torch.empty((T * k, w.H), dtype=torch.bfloat16, device=x.device)
+    sa = sas = sy = None
+    if with_shared and w.shared_I > 0:
+        sa, sas = _act_tensors(T, w.shared_I, w.fmt, x.device)
+        sy = torch.empty((T, w.H), dtype=torch.bfloat16, device=x.device)
+    _dev(x, x_scales, sorted_pair, offsets, act, act_scales, y, sa, sas, sy)
+    ws = w.c_struct()
+    _check("moe_grouped_ffn", load().moe_grouped_ffn(
+        _c.byref(ws), _ptr(x), _ptr(x_scales), T, k, _ptr(sorted_pair), _ptr(offsets), _ptr(act),
+        _ptr(act_scales), _ptr(y), _ptr(sa), _ptr(sas), _ptr(sy), _stream()))
+    return act, act_scales, y, sa, sas, sy
+
+
 def combine(y, pair_pos, topk_w, shared_y, out=None):
     T, k = topk_w.shape
     H = y.shape[1]

@@ -145,6 +145,74 @@ GroupedGemm routed_gemm(const MoeFfnWeights* w, int T, int k, const int32_t* sor
   return g;
 }
 
+GroupedGemm up_gemm(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales, int T, int k,
+                    const int32_t* sorted_pair, const int32_t* offsets, void* act, uint8_t* act_scales) {
+  GroupedGemm g = routed_gemm(w, T, k, sorted_pair, offsets);
+  g.A = x;
+  g.A_scales = x_scales;
+  g.gather = 1;
+  g.W = w->w13;
+  g.W_scales = w->w13_scales;
+  g.N = w->I;
+  g.K = w->H;
+  g.up_off = w->I;
+  g.out = act;
+  g.out_scales = act_scales;
+  if (w->fmt == MOE_FMT_W4A8) {
+    g.w_gstride = (long long)w->I * w->H;  // bytes: 2I rows of H/2
+    g.ws_gstride = (long long)moe::mx_packed_scales_bytes(2 * w->I, w->H);
+  } else {
+    g.w_gstride = 2ll * w->I * w->H;
+  }
+  return g;
+}
+
+GroupedGemm down_gemm(const MoeFfnWeights* w, const void* act, const uint8_t* act_scales, int T, int k,
+                      const int32_t* offsets, uint16_t* y) {
+  GroupedGemm g = routed_gemm(w, T, k, nullptr, offsets);
+  g.A = act;
+  g.A_scales = act_scales;
+  g.gather = 0;
+  g.W = w->w2;
+  g.W_scales = w->w2_scales;
+  g.N = w->H;
+  g.K = w->I;
+  g.up_off = 0;
+  g.out = y;
+  if (w->fmt == MOE_FMT_W4A8) {
+    g.w_gstride = (long long)w->H * (w->I / 2);
+    g.ws_gstride = (long long)moe::mx_packed_scales_bytes(w->H, w->I);
+  } else {
+    g.w_gstride = (long long)w->H * w->I;
+  }
+  return g;
+}
+
+// The shared expert run inside the routed grouped GEMMs as one more group
+// ([Hy3] section 1.1: one always-on shared expert; the survey of this layer
+// plans it as an extra group of the grouped matmul): its T rows read x (and
+// then its own activations) without gather and its tiles join the routed
+// tile list, so no separate, partly empty launch runs after the routed ones.
+// Taken for bf16 weights with shared_I == I when both GEMMs run on the
+// LDS-tiled kernels (many rows per expert); else the caller launches the
+// shared expert on its own.  Fills the extra-group fields of up / dn.
+bool fold_shared(const MoeFfnWeights* w, int T, int k, const void* x, void* shared_act,
+                 uint16_t* shared_y, GroupedGemm& up, GroupedGemm& dn) {
+  if (w->fmt != MOE_FMT_BF16 || w->shared_I <= 0 || w->shared_I != w->I) return false;
+  if (small_m((long long)T * k, w->E)) return false;
+  up.xg_rows = T;
+  up.xg_A = x;
+  up.xg_W = w->shared_w13;
+  up.xg_out = shared_act;
+  dn.xg_rows = T;
+  dn.xg_A = shared_act;
+  dn.xg_W = w->shared_w2;
+  dn.xg_out = shared_y;
+  if (moe::tiled4_fits(up, true) && moe::tiled4_fits(dn, false)) return true;
+  up.xg_rows = dn.xg_rows = 0;
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -283,24 +351,10 @@ int moe_grouped_ffn_up(const MoeFfnWeights* w, const void* x, const uint8_t* x_s
   if ((st = check_ptrs({x, sorted_pair, offsets, act}))) return st;
   const bool mx = w->fmt == MOE_FMT_W4A8;
   if (mx && (st = check_ptrs({x_scales, act_scales}))) return st;
-  GroupedGemm g = routed_gemm(w, T, k, sorted_pair, offsets);
-  g.A = x;
-  g.A_scales = x_scales;
-  g.gather = 1;
-  g.W = w->w13;
-  g.W_scales = w->w13_scales;
-  g.N = w->I;
-  g.K = w->H;
-  g.up_off = w->I;
-  g.out = act;
-  g.out_scales = act_scales;
-  if (mx) {
-    g.w_gstride = (long long)w->I * w->H;  // bytes: 2I rows of H/2
-    g.ws_gstride = (long long)moe::mx_packed_scales_bytes(2 * w->I, w->H);
-    return moe::launch_ffn_up_w4a8(g, small_m((long long)T * k, w->E), as_stream(stream));
-  }
-  g.w_gstride = 2ll * w->I * w->H;
-  return moe::launch_ffn_up_bf16(g, small_m((long long)T * k, w->E), as_stream(stream));
+  const GroupedGemm g = up_gemm(w, x, x_scales, T, k, sorted_pair, offsets, act, act_scales);
+  const bool sm = small_m((long long)T * k, w->E);
+  return mx ? moe::launch_ffn_up_w4a8(g, sm, as_stream(stream))
+            : moe::launch_ffn_up_bf16(g, sm, as_stream(stream));
 }
 
 int moe_grouped_ffn_down(const MoeFfnWeights* w, const void* act, const uint8_t* act_scales,
@@ -313,23 +367,10 @@ int moe_grouped_ffn_down(const MoeFfnWeights* w, const void* act, const uint8_t*
   if ((st = check_ptrs({act, offsets, y}))) return st;
   const bool mx = w->fmt == MOE_FMT_W4A8;
   if (mx && (st = check_ptrs({act_scales}))) return st;
-  GroupedGemm g = routed_gemm(w, T, k, nullptr, offsets);
-  g.A = act;
-  g.A_scales = act_scales;
-  g.gather = 0;
-  g.W = w->w2;
-  g.W_scales = w->w2_scales;
-  g.N = w->H;
-  g.K = w->I;
-  g.up_off = 0;
-  g.out = y;
-  if (mx) {
-    g.w_gstride = (long long)w->H * (w->I / 2);
-    g.ws_gstride = (long long)moe::mx_packed_scales_bytes(w->H, w->I);
-    return moe::launch_ffn_down_w4a8(g, small_m((long long)T * k, w->E), as_stream(stream));
-  }
-  g.w_gstride = (long long)w->H * w->I;
-  return moe::launch_ffn_down_bf16(g, small_m((long long)T * k, w->E), as_stream(stream));
+  const GroupedGemm g = down_gemm(w, act, act_scales, T, k, offsets, y);
+  const bool sm = small_m((long long)T * k, w->E);
+  return mx ? moe::launch_ffn_down_w4a8(g, sm, as_stream(stream))
+            : moe::launch_ffn_down_bf16(g, sm, as_stream(stream));
 }
 
 int moe_shared_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales, int T,
@@ -380,6 +421,19 @@ int moe_grouped_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scal
                     const int32_t* sorted_pair, const int32_t* offsets, void* act,
                     uint8_t* act_scales, uint16_t* y, void* shared_act,
                     uint8_t* shared_act_scales, uint16_t* shared_y, void* stream) {
+  if (w != nullptr && w->shared_I > 0 && shared_y != nullptr && T > 0 && check_weights(w) == MOE_OK &&
+      check_k(w->E, k) == MOE_OK && check_rows(T, k) == MOE_OK &&
+      check_ptrs({x, sorted_pair, offsets, act, y, shared_act, shared_y}) == MOE_OK) {
+    GroupedGemm up = up_gemm(w, x, x_scales, T, k, sorted_pair, offsets, act, act_scales);
+    GroupedGemm dn = down_gemm(w, act, act_scales, T, k, offsets, y);
+    if (fold_shared(w, T, k, x, shared_act, shared_y, up, dn)) {
+      moe::launch_tiled4(up, true, as_stream(stream));
+      int st = moe::launch_status();
+      if (st) return st;
+      moe::launch_tiled4(dn, false, as_stream(stream));
+      return moe::launch_status();
+    }
+  }
   int st = moe_grouped_ffn_up(w, x, x_scales, T, k, sorted_pair, offsets, act, act_scales, stream);
   if (st) return st;
   st = moe_grouped_ffn_down(w, act, act_scales, T, k, offsets, y, stream);
@@ -504,16 +558,28 @@ int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t*
   hipEvent_t ev0 = reinterpret_cast<hipEvent_t>(b->ev_ffn_up_begin);
   hipEvent_t ev1 = reinterpret_cast<hipEvent_t>(b->ev_ffn_up_end);
   const bool timed = ev0 != nullptr && ev1 != nullptr;
+  GroupedGemm up = up_gemm(&d->ffn, xin, xin_s, T, k, b->sorted_pair, b->offsets, b->act, b->act_scales);
+  GroupedGemm dn = down_gemm(&d->ffn, b->act, b->act_scales, T, k, b->offsets, b->y);
+  const bool folded = shared && fold_shared(&d->ffn, T, k, xin, b->shared_act, b->shared_y, up, dn);
   if (timed && hipEventRecord(ev0, as_stream(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
-  if ((st = moe_grouped_ffn_up(&d->ffn, xin, xin_s, T, k, b->sorted_pair, b->offsets, b->act,
-                               b->act_scales, stream)))
+  if (folded) {
+    moe::launch_tiled4(up, true, as_stream(stream));
+    if ((st = moe::launch_status())) return st;
+  } else if ((st = moe_grouped_ffn_up(&d->ffn, xin, xin_s, T, k, b->sorted_pair, b->offsets, b->act,
+                                      b->act_scales, stream))) {
     return st;
+  }
   if (timed && hipEventRecord(ev1, as_stream(stream)) != hipSuccess) return MOE_ERR_LAUNCH;
-  if ((st = moe_grouped_ffn_down(&d->ffn, b->act, b->act_scales, T, k, b->offsets, b->y, stream)))
-    return st;
-  if (shared && (st = moe_shared_ffn(&d->ffn, xin, xin_s, T, b->shared_act, b->shared_act_scales,
-                                     b->shared_y, stream)))
-    return st;
+  if (folded) {
+    moe::launch_tiled4(dn, false, as_stream(stream));
+    if ((st = moe::launch_status())) return st;
+  } else {
+    if ((st = moe_grouped_ffn_down(&d->ffn, b->act, b->act_scales, T, k, b->offsets, b->y, stream)))
+      return st;
+    if (shared && (st = moe_shared_ffn(&d->ffn, xin, xin_s, T, b->shared_act, b->shared_act_scales,
+                                       b->shared_y, stream)))
+      return st;
+  }
   return moe_combine(b->y, b->pair_pos, b->topk_w, shared ? b->shared_y : nullptr, T, k, d->H,
                      out, stream);
 }

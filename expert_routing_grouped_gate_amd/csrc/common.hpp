@@ -118,8 +118,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // up to 5 consecutive groups, all loads independent), counts the tiles and
 // scans them across the wave; find() maps an m-tile index to (group, first
 // row, valid rows) from registers only.  When offsets == nullptr there is a
-// single group of `ident_rows` rows starting at row 0.  Every lane of the wave
-// holds the same results; no LDS and no barrier are used.
+// single group of `ident_rows` rows starting at row 0.  With extra_rows > 0
+// one more group G follows the G groups of `offsets`: rows [offsets[G],
+// offsets[G] + extra_rows) (the shared expert run in the same launch).
+// Every lane of the wave holds the same results; no LDS and no barrier are
+// used.
 struct TileMap {
   int per, gbeg, excl, total, BM;
   int o[6];      // offsets[gbeg .. gbeg + per] (clamped)
@@ -130,7 +133,7 @@ struct TileMap {
   // Offsets are clamped to [0, max_rows] (max_rows: rows the output can
   // hold), so even malformed offsets yield tiles inside the buffers.
   __device__ __forceinline__ void init(const int* __restrict__ offs, int G, int ident, int bm,
-                                       int max_rows) {
+                                       int max_rows, int extra_rows = 0) {
     offsets = offs;
     ident_rows = ident;
     BM = bm;
@@ -139,14 +142,18 @@ struct TileMap {
       return;
     }
     const int lane = threadIdx.x & 63;
-    per = (G + 63) >> 6;
+    const int Gt = G + (extra_rows > 0 ? 1 : 0);
+    per = (Gt + 63) >> 6;
     gbeg = lane * per;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) o[i] = min(max(offs[min(gbeg + i, G)], 0), max_rows);
+    for (int i = 0; i < 6; ++i) {
+      const int j = gbeg + i;
+      o[i] = min(max(offs[min(j, G)], 0), max_rows) + (j > G ? extra_rows : 0);
+    }
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
-      const int t = (i < per && gbeg + i < G) ? max(o[i + 1] - o[i] + bm - 1, 0) / bm : 0;
+      const int t = (i < per && gbeg + i < Gt) ? max(o[i + 1] - o[i] + bm - 1, 0) / bm : 0;
       tiles[i] = t;
       sum += t;
     }
@@ -259,9 +266,10 @@ __device__ __forceinline__ TileMap unpark_tilemap(const int* slot, const int* of
   return tl;
 }
 
-// One output tile of a grouped GEMM (wave-uniform).
+// One output tile of a grouped GEMM (wave-uniform); grow0 = its group's
+// first row.
 struct TileRef {
-  int grp, n_tile, row0, nrows;
+  int grp, n_tile, row0, nrows, grow0;
 };
 
 // Tile `id` (after xcd_remap) of the expert-major order: group, then n-tile,
@@ -279,6 +287,7 @@ __device__ __forceinline__ TileRef expert_major_tile(const TileMap& tl, int id, 
   r.n_tile = __builtin_amdgcn_readfirstlane(n_tile);
   r.row0 = __builtin_amdgcn_readfirstlane(row0);
   r.nrows = __builtin_amdgcn_readfirstlane(min(tl.BM, grow1 - row0));
+  r.grow0 = __builtin_amdgcn_readfirstlane(grow0);
   return r;
 }
 

@@ -70,6 +70,14 @@ struct GroupedGemm {
   int up_off;                 // SwiGLU: row offset of the up half in W (= N)
   void* out;                  // [rows, N] bf16, or MXFP8 codes (W4A8 GEMM1)
   uint8_t* out_scales;        // [rows, N/32] (W4A8 GEMM1)
+  // One extra group after the G groups of `offsets` (the shared expert in
+  // the routed launch; LDS-tiled bf16 kernels only): xg_rows rows that read
+  // activation rows 0.. of xg_A without gather, multiply by xg_W (same shape
+  // as one group's W) and write rows 0.. of xg_out.  0 rows: none.
+  int xg_rows;
+  const void* xg_A;
+  const void* xg_W;
+  void* xg_out;
 };
 
 int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s);
@@ -79,10 +87,12 @@ int launch_ffn_down_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s);
 // LDS-tiled W4A8 GEMMs (128 x 256 block tiles) and the shapes they take.
 bool mx_tiled_fits(const GroupedGemm& g, bool swiglu);
 void launch_mx_tiled(const GroupedGemm& g, bool swiglu, hipStream_t s);
-// bf16 GEMMs for many rows per expert on one wave per SIMD (128 x 256 block
-// tiles, a DMA ring streaming across tiles) and the shapes they take.
+// bf16 GEMMs for many rows per expert on two waves per SIMD (128 x 256 block
+// tiles on eight waves, a DMA ring streaming across tiles) and the shapes
+// they take.
 bool tiled4_fits(const GroupedGemm& g, bool swiglu);
 void launch_tiled4(const GroupedGemm& g, bool swiglu, hipStream_t s);
+
 
 int launch_mx_quantize(const uint16_t* x, int rows, int cols, uint8_t* codes, uint8_t* scales,
                        hipStream_t s);

@@ -1,5 +1,5 @@
 // S5/S6 for experts with many rows (prefill): bf16 grouped GEMMs on
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation, one wave per SIMD.
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation, two waves per SIMD.
 //
 // [Qwen3] "GMM enablement and routing optimisation": one grouped matmul over
 // all experts; "MoE TP optimisation -> compute decomposition": w13 = gate
@@ -10,8 +10,12 @@
 //
 // Block tile: BM = 128 activation rows x BN = 256 weight rows (GEMM1: the 128
 // gate rows n0.. and the matching 128 up rows, 128 output columns; GEMM2: 256
-// output columns), K step 64.  Four waves (2 x 2), each a 64 x 128 sub-tile
-// of 4 x 8 MFMAs whose accumulators (128 per lane) live in AGPRs.  One LDS
+// output columns), K step 64.  Eight waves (2 x 4, two per SIMD), each a
+// 64 x 64 sub-tile of 4 x 4 MFMAs (64 fp32 accumulators per lane).  Copies
+// into LDS are issued per wave, and eight issuing waves move more of them
+// per CU than four (measured on L2-resident data: ~91 against ~56 B/ns per
+// CU); rows stay 128 B per stage, since a 64 B row slice doubles the cache
+// lines each 1 KB copy touches and fills the texture address queue.  One LDS
 // stage (48 KB) holds the step's 128 activation rows then 256 weight rows,
 // 128 B each, the 16-byte chunk c of row r at chunk c ^ (r & 7).  Stages are
 // filled by buffer loads to LDS (DMA): each wave instruction writes 1 KB = 8
@@ -33,21 +37,22 @@ namespace moe {
 
 template <bool SWIGLU>
 struct Tiled4 {
-  static constexpr int BM = 128, BN = 256, WM = 2, WN = 2, NW = 4, NTHR = 256;
+  static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, NW = 8, NTHR = 512;
   static constexpr int MT = BM / 16 / WM;  // activation groups per wave (4)
-  static constexpr int NT = BN / 16 / WN;  // weight groups per wave (8)
+  static constexpr int NT = BN / 16 / WN;  // weight groups per wave (4)
   static constexpr int BNOUT = SWIGLU ? BN / 2 : BN;
   static constexpr int ABYTES = BM * 128;
   static constexpr int STAGE = (BM + BN) * 128;  // bytes
   static constexpr int NS = 3;
-  static constexpr int LPA = BM / 8 / NW;  // 1 KB activation DMAs per wave per stage (4)
-  static constexpr int LPB = BN / 8 / NW;  // 1 KB weight DMAs per wave per stage (8)
+  static constexpr int LPA = BM / 8 / NW;  // 1 KB activation DMAs per wave per stage (2)
+  static constexpr int LPB = BN / 8 / NW;  // 1 KB weight DMAs per wave per stage (4)
   static constexpr int LPW = LPA + LPB;
-  static_assert(NS * STAGE + NW * kTileMapWords * 64 * 4 <= 160 * 1024, "LDS");
+  static_assert(NS * STAGE <= 160 * 1024, "LDS");
 };
 
 struct T4Tile {
   int grp, n0, row0, nrows;  // wave-uniform
+  int ext, rel0;             // the extra (shared-expert) group; its first row relative to the group
 };
 
 // Half-step fragments: MT activation and NT weight operands of 16 B.
@@ -62,15 +67,15 @@ struct Frags {
 // made the compiler drain every load before the move): activation row of
 // sorted row r is the token of pair sorted_pair[r], else r itself.
 template <bool SWIGLU, bool GATHER>
-__global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles) {
+__global__ __launch_bounds__(512, 1) void ffn_tiled4(GroupedGemm g, int n_tiles) {
   using C = Tiled4<SWIGLU>;
   constexpr int MT = C::MT, NT = C::NT, NW = C::NW;
-  // One LDS array: the ring, then the scheduler's per-lane table (one copy
-  // per wave, park_tilemap).  (A second __shared__ variable makes the
-  // compiler wait for every outstanding DMA before each LDS read.)
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE + NW * kTileMapWords * 64 * 4];
+  // One LDS array, the ring (a second __shared__ variable makes the compiler
+  // wait for every outstanding DMA before each LDS read); the scheduler's
+  // table stays in registers.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
   TileMap tm;
-  tm.init(g.offsets, g.G, g.ident_rows, C::BM, g.total_rows);
+  tm.init(g.offsets, g.G, g.ident_rows, C::BM, g.total_rows, g.xg_rows);
   const int total = __builtin_amdgcn_readfirstlane(tm.total * n_tiles);
   int t = blockIdx.x;
   if (t >= total) return;  // uniform per block: no barrier is left waiting
@@ -78,33 +83,37 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int* const tm_slot = reinterpret_cast<int*>(smem + C::NS * C::STAGE) + wave * kTileMapWords * 64;
-  if (g.offsets != nullptr) park_tilemap(tm, tm_slot);
   const int wm = wave % C::WM, wn = wave / C::WM;
   const int li = lane & 15, kc = lane >> 4;
   const int K = g.K, nk = K / 64;  // nk >= 5 (launcher)
   const uint32_t rowb = 2u * (uint32_t)K;  // bytes per row
   const int arows_total = GATHER ? g.total_rows / g.topk : g.total_rows;
   const __amdgpu_buffer_rsrc_t ar = mx_rsrc(g.A, (uint32_t)arows_total * rowb);
+  // the extra group's activations (identity rows, no gather)
+  const __amdgpu_buffer_rsrc_t arx = mx_rsrc(g.xg_rows > 0 ? g.xg_A : g.A, (uint32_t)g.xg_rows * rowb);
   const uint32_t wrows = SWIGLU ? 2u * (uint32_t)g.up_off : (uint32_t)g.N;
   const uint32_t wbytes = wrows * rowb;
   const uint32_t dchunk = 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
 
   auto locate = [&](int tt) {
-    const TileMap tl = unpark_tilemap(tm_slot, g.offsets, g.ident_rows, tm.total, C::BM);
-    const TileRef r = expert_major_tile(tl, xcd_remap(tt, total), n_tiles);
+    const TileRef r = expert_major_tile(tm, xcd_remap(tt, total), n_tiles);
     T4Tile ti;
     ti.grp = r.grp;
     ti.n0 = __builtin_amdgcn_readfirstlane(r.n_tile * C::BNOUT);
     ti.row0 = r.row0;
     ti.nrows = r.nrows;
+    ti.ext = __builtin_amdgcn_readfirstlane(g.xg_rows > 0 && r.grp == g.G ? 1 : 0);
+    ti.rel0 = __builtin_amdgcn_readfirstlane(r.row0 - r.grow0);
     return ti;
   };
   // Activation rows of this lane's LPA DMAs (group ra = wave + NW i, 8 rows;
   // lane l fills row 8 ra + l / 8), in two halves so that no loaded value is
   // used right after its load: gather_issue loads the pair ids (rows past the
   // tile end reuse a valid row), gather_finish turns them into byte offsets
-  // of the rows' step-0 chunk (pair ids clamped into the token range).
+  // of the rows' step-0 chunk (pair ids clamped into the token range).  The
+  // extra group's rows are its own row indices (the pair ids loaded for them,
+  // from a clamped index, go unused: selects, not branches, keep the two
+  // kinds of tile on one path).
   auto tile_rows = [&](const T4Tile& ti, int* r) {
 #pragma unroll
     for (int i = 0; i < C::LPA; ++i) r[i] = ti.row0 + min(8 * (wave + NW * i) + (lane >> 3), ti.nrows - 1);
@@ -114,12 +123,13 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
       int r[C::LPA];
       tile_rows(ti, r);
 #pragma unroll
-      for (int i = 0; i < C::LPA; ++i) raw[i] = g.sorted_pair[r[i]];
+      for (int i = 0; i < C::LPA; ++i) raw[i] = g.sorted_pair[min(r[i], g.total_rows - 1)];
     }
   };
   // Rows past the tile end get an offset past the end of A: the buffer load
   // returns zeros without touching memory (those rows are never stored).
   const uint32_t a_oob = (uint32_t)arows_total * rowb;
+  const uint32_t ax_oob = (uint32_t)g.xg_rows * rowb;
   auto gather_finish = [&](const T4Tile& ti, const int* raw, uint32_t* adma) {
     int r[C::LPA];
     tile_rows(ti, r);
@@ -127,8 +137,9 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
     for (int i = 0; i < C::LPA; ++i) {
       const uint32_t arow = GATHER ? (uint32_t)min(max(raw[i], 0) / g.topk, arows_total - 1)
                                    : (uint32_t)r[i];
+      const uint32_t xrow = (uint32_t)(r[i] - ti.row0 + ti.rel0);
       const bool pad = 8 * (wave + NW * i) + (lane >> 3) >= ti.nrows;
-      adma[i] = pad ? a_oob : arow * rowb + dchunk;
+      adma[i] = pad ? (ti.ext ? ax_oob : a_oob) : (ti.ext ? xrow : arow) * rowb + dchunk;
     }
   };
   // Weight rows of this lane's LPB DMAs relative to the tile's n0 (group rb =
@@ -146,13 +157,15 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   // int: an unsigned argument made the host pass drop the kernel's stub.)
   auto issue = [&](const T4Tile& ti, const uint32_t* adma, int buf, int st) {
     uint8_t* stg = smem + buf * C::STAGE;
-    const __amdgpu_buffer_rsrc_t wr = mx_rsrc(Wbase + (size_t)ti.grp * g.w_gstride, wbytes);
+    const __amdgpu_buffer_rsrc_t wr =
+        mx_rsrc(ti.ext ? g.xg_W : static_cast<const void*>(Wbase + (size_t)ti.grp * g.w_gstride), wbytes);
+    const __amdgpu_buffer_rsrc_t a_r = ti.ext ? arx : ar;
     const uint32_t aso = (uint32_t)st * 128u;
     const uint32_t wso = (uint32_t)ti.n0 * rowb + aso;
 #pragma unroll
     for (int i = 0; i < C::LPA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ar, (__attribute__((address_space(3))) void*)(stg + (wave + NW * i) * 1024), 16, (int)adma[i],
+          a_r, (__attribute__((address_space(3))) void*)(stg + (wave + NW * i) * 1024), 16, (int)adma[i],
           (int)aso, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::LPB; ++i)
@@ -171,7 +184,7 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   for (int h = 0; h < 2; ++h) {
     const int ch = 16 * ((4 * h + kc) ^ (li & 7));
     aoff[h] = (64 * wm + li) * 128 + ch;
-    boff[h] = C::ABYTES + ((SWIGLU ? 64 : 128) * wn + li) * 128 + ch;
+    boff[h] = C::ABYTES + ((SWIGLU ? C::BN / 2 : C::BN) / C::WN * wn + li) * 128 + ch;
   }
   auto bgroup = [](int ni) {
     if (SWIGLU) return ni < NT / 2 ? ni * 2048 : (C::BN / 2) * 128 + (ni - NT / 2) * 2048;
@@ -281,14 +294,16 @@ __global__ __launch_bounds__(256, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
     // halves (v_permlane16_swap), so that an even-kc lane holds 8 consecutive
     // columns of group ni and its odd partner 8 of group ni + 1: one 16-byte
     // store per lane and pair instead of two 8-byte ones.
-    uint16_t* out = static_cast<uint16_t*>(g.out);
+    // the extra group's rows go to its own output, row rel0 + r
+    uint16_t* out = static_cast<uint16_t*>(cur.ext ? g.xg_out : g.out);
+    const int orow0 = cur.ext ? cur.rel0 : cur.row0;
     constexpr int NG = SWIGLU ? NT / 2 : NT;  // output groups per wave
     const int odd = kc & 1;
-    const int col = (SWIGLU ? 64 : 128) * wn + 8 * (kc >> 1);
+    const int col = (SWIGLU ? C::BN / 2 : C::BN) / C::WN * wn + 8 * (kc >> 1);
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
       const int r = 64 * wm + 16 * mi + li;
-      uint16_t* orow = out + (size_t)(cur.row0 + min(r, cur.nrows - 1)) * g.N + cur.n0 + col;
+      uint16_t* orow = out + (size_t)(orow0 + min(r, cur.nrows - 1)) * g.N + cur.n0 + col;
 #pragma unroll
       for (int np = 0; np < NG; np += 2) {
         u32x2 pk[2];
@@ -333,7 +348,8 @@ bool tiled4_fits(const GroupedGemm& g, bool swiglu) {
   const long long arows = g.gather ? g.total_rows / g.topk : g.total_rows;
   const long long wrows = swiglu ? 2ll * g.up_off : g.N;
   return g.N % (swiglu ? 128 : 256) == 0 && g.K % 64 == 0 && g.K >= 320 &&
-         arows * g.K * 2 < (1ll << 32) && wrows * g.K * 2 < (1ll << 32);
+         arows * g.K * 2 < (1ll << 32) && wrows * g.K * 2 < (1ll << 32) &&
+         (long long)g.xg_rows * g.K * 2 < (1ll << 32);
 }
 
 template <bool SWIGLU, bool GATHER>
@@ -341,7 +357,8 @@ static void launch_tiled4_impl(const GroupedGemm& g, hipStream_t s) {
   using C = Tiled4<SWIGLU>;
   const int nt = g.N / C::BNOUT;
   const int groups = g.offsets ? g.G : 1;
-  const long long bound = ((long long)(g.total_rows + C::BM - 1) / C::BM + groups) * nt;
+  const long long bound =
+      ((long long)(g.total_rows + g.xg_rows + C::BM - 1) / C::BM + groups + (g.xg_rows > 0)) * nt;
   auto k = ffn_tiled4<SWIGLU, GATHER>;
   const int grid = resident_grid(reinterpret_cast<const void*>(k), C::NTHR, bound);
   hipLaunchKernelGGL(k, dim3(grid), dim3(C::NTHR), 0, s, g, nt);

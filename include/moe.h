@@ -287,7 +287,10 @@ int moe_shared_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scale
                    void* stream);
 
 /* moe_grouped_ffn_up followed by moe_grouped_ffn_down (and moe_shared_ffn
- * when w->shared_I > 0 and shared_y is not NULL). */
+ * when w->shared_I > 0 and shared_y is not NULL).  With bf16 weights,
+ * shared_I == I and many rows per expert (T * k > 16 * E), the shared expert
+ * runs as one more group inside the two routed launches; every output equals
+ * the separate calls' bit for bit. */
 int moe_grouped_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales,
                     int T, int k, const int32_t* sorted_pair, const int32_t* offsets,
                     void* act, uint8_t* act_scales, uint16_t* y,
@@ -310,7 +313,9 @@ int moe_combine(const uint16_t* y, const int32_t* pair_pos, const float* topk_w,
  * S0..S7 in one call on one stream.  With T <= 16 and T*k <= 1024 (decode)
  * the front end is two launches: router partial sums (which also write the
  * MXFP8 x of the W4A8 path) and one block for logits, top-k, counts and the
- * permutation; the buffers receive the same values as the per-step calls. */
+ * permutation; the shared expert runs inside the routed GEMM launches as
+ * moe_grouped_ffn describes; the buffers receive the same values as the
+ * per-step calls. */
 typedef struct {
   int H, E, k;
   int gate_mode;        /* moe_gate_mode */

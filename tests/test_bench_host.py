@@ -47,6 +47,15 @@ def test_hy3_adds_the_shared_expert_and_bias():
     assert w["layer_bytes"] == (155 * 37_748_736 + shared + 192 * 4096 * 4 + 192 * 4
                                 + 2 * 4096 * 4096 * 2)
     assert w["flops"] == 1_236_950_581_248 + 2 * 4096 * 3 * 1536 * 4096   # 1.3916 TFLOP
+    # the shared expert runs inside the GEMM1 launch: its w13 (2 x 1536 x 4096
+    # bf16) is read, its 4096 x 1536 bf16 activations written, its flops done
+    assert w["g1_shared"]
+    assert w["g1_bytes"] == (155 * 25_165_824 + 4096 * 4096 * 2 + 4096 * 8 * 1536 * 2
+                             + 25_165_824 + 4096 * 1536 * 2)
+    assert w["g1_flops"] == 824_633_720_832 + 2 * 4096 * 2 * 1536 * 4096
+    # not folded: decode-sized rows per expert, or no shared expert
+    assert not bench.workload_bytes_flops(W.CONFIGS["hy3"].with_(T=16), counts_touching(192, 80))["g1_shared"]
+    assert not bench.workload_bytes_flops(W.CONFIGS["qwen3_prefill"], counts_touching(128, 128))["g1_shared"]
 
 
 def test_w4a8_bytes():

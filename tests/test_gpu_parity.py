@@ -206,6 +206,32 @@ def test_grouped_ffn_rows(name):
     _ffn_check(name)
 
 
+@pytest.mark.parametrize("name", ["tiled4_hy3", "hy3_full"])
+def test_shared_expert_in_the_routed_launch_equals_its_own(name):
+    """With bf16 weights, shared_I == I and many rows per expert, the layer
+    and moe_grouped_ffn run the shared expert as one more group of the
+    routed GEMM launches.  Its rows must equal moe_shared_ffn's (its own
+    launches) bit for bit, and the routed rows moe_grouped_ffn_up/_down's:
+    every row runs the same MFMAs over the same K-steps either way."""
+    cfg = CFG["hy3"] if name == "hy3_full" else SMALL[name]
+    L = get_layer(cfg)
+    c = L.cfg
+    assert c.shared_I == c.I and c.T * c.k > 16 * c.E       # the folded case
+    layer = L.layer()
+    layer.forward(L.dev["x"])
+    b = layer.buf
+    act, _, y, sa, _, sy = B.grouped_ffn(L.weights, L.dev["x"], None, c.k, b["sorted_pair"], b["offsets"])
+    sa_own, _, sy_own = B.shared_ffn(L.weights, L.dev["x"])
+    act_own, _ = B.grouped_ffn_up(L.weights, L.dev["x"], None, c.k, b["sorted_pair"], b["offsets"])
+    y_own = B.grouped_ffn_down(L.weights, act_own, None, c.T, c.k, b["offsets"])
+    torch.cuda.synchronize()
+    for folded in ((b["shared_act"], b["shared_y"]), (sa, sy)):
+        assert torch.equal(folded[0], sa_own) and torch.equal(folded[1], sy_own)
+    n = int(b["offsets"][c.E])
+    assert torch.equal(b["act"][:n], act_own[:n]) and torch.equal(act[:n], act_own[:n])
+    assert torch.equal(b["y"][:n], y_own[:n]) and torch.equal(y[:n], y_own[:n])
+
+
 @pytest.mark.parametrize("name", ["small_hy3", "small_hy3_decode", "tiled4_hy3"])
 def test_shared_ffn(name):
     L = get_layer(SMALL[name])
