@@ -130,8 +130,26 @@ int check_weights(const MoeFfnWeights* w) {
   return MOE_ERR_UNSUPPORTED;
 }
 
-// Few rows per expert -> the weight-streaming (skinny) tiles.
-inline bool small_m(long long rows, int groups) { return rows <= 16ll * groups; }
+// The weight-streaming GEMMs (16-row tiles, weights straight into MFMA
+// operands) or the LDS-tiled ones (128-row tiles).  With at most 16 tokens
+// no expert holds more than 16 rows, so streaming reads each touched
+// expert's weights exactly once.  Above that the choice follows the
+// crossover measured on full-size layers (H = 4096, I = 1536, 128 and 192
+// experts, top-8; both paths forced, layer time): bf16 streaming is faster
+// up to about 3 rows per expert on average and W4A8 streaming up to about 8
+// (each 16-row tile re-reads its expert's weights, but a 128-row W4A8 tile
+// costs more MFMA time per padded row than the packed weights take to
+// stream); with a bf16 shared expert that the tiled launches take in as one
+// more group (fold_shared) the tiled path is faster from 17 tokens on.  The
+// choice depends on the weights and T, k only, so the folded launches and
+// the separate per-GEMM calls always run the same kernels.
+inline bool stream_rows(const MoeFfnWeights* w, int T, int k) {
+  if (T <= 16) return true;
+  const long long rows = (long long)T * k;
+  if (w->fmt == MOE_FMT_W4A8) return rows <= 8ll * w->E;
+  const bool shared_folds = w->shared_I > 0 && w->shared_I == w->I;
+  return !shared_folds && rows <= 3ll * w->E;
+}
 
 GroupedGemm routed_gemm(const MoeFfnWeights* w, int T, int k, const int32_t* sorted_pair,
                         const int32_t* offsets) {
@@ -194,12 +212,12 @@ GroupedGemm down_gemm(const MoeFfnWeights* w, const void* act, const uint8_t* ac
 // then its own activations) without gather and its tiles join the routed
 // tile list, so no separate, partly empty launch runs after the routed ones.
 // Taken for bf16 weights with shared_I == I when both GEMMs run on the
-// LDS-tiled kernels (many rows per expert); else the caller launches the
+// LDS-tiled kernels (more than 16 tokens); else the caller launches the
 // shared expert on its own.  Fills the extra-group fields of up / dn.
 bool fold_shared(const MoeFfnWeights* w, int T, int k, const void* x, void* shared_act,
                  uint16_t* shared_y, GroupedGemm& up, GroupedGemm& dn) {
   if (w->fmt != MOE_FMT_BF16 || w->shared_I <= 0 || w->shared_I != w->I) return false;
-  if (small_m((long long)T * k, w->E)) return false;
+  if (stream_rows(w, T, k)) return false;
   up.xg_rows = T;
   up.xg_A = x;
   up.xg_W = w->shared_w13;
@@ -352,7 +370,7 @@ int moe_grouped_ffn_up(const MoeFfnWeights* w, const void* x, const uint8_t* x_s
   const bool mx = w->fmt == MOE_FMT_W4A8;
   if (mx && (st = check_ptrs({x_scales, act_scales}))) return st;
   const GroupedGemm g = up_gemm(w, x, x_scales, T, k, sorted_pair, offsets, act, act_scales);
-  const bool sm = small_m((long long)T * k, w->E);
+  const bool sm = stream_rows(w, T, k);
   return mx ? moe::launch_ffn_up_w4a8(g, sm, as_stream(stream))
             : moe::launch_ffn_up_bf16(g, sm, as_stream(stream));
 }
@@ -368,7 +386,7 @@ int moe_grouped_ffn_down(const MoeFfnWeights* w, const void* act, const uint8_t*
   const bool mx = w->fmt == MOE_FMT_W4A8;
   if (mx && (st = check_ptrs({act_scales}))) return st;
   const GroupedGemm g = down_gemm(w, act, act_scales, T, k, offsets, y);
-  const bool sm = small_m((long long)T * k, w->E);
+  const bool sm = stream_rows(w, T, k);
   return mx ? moe::launch_ffn_down_w4a8(g, sm, as_stream(stream))
             : moe::launch_ffn_down_bf16(g, sm, as_stream(stream));
 }

@@ -381,8 +381,8 @@ static void launch_tiled(const GroupedGemm& g, hipStream_t s) {
   hipLaunchKernelGGL(k, dim3(grid), dim3(64 * WM * WN), 0, s, g, nt);
 }
 
-int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
-  if (small_m)
+int launch_ffn_up_bf16(const GroupedGemm& g, bool streamed, hipStream_t s) {
+  if (streamed)
     launch_skinny<true, 1, 4, 4>(g, s);
   else if (tiled4_fits(g, true))
     launch_tiled4(g, true, s);
@@ -391,8 +391,8 @@ int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
   return launch_status();
 }
 
-int launch_ffn_down_bf16(const GroupedGemm& g, bool small_m, hipStream_t s) {
-  if (small_m)
+int launch_ffn_down_bf16(const GroupedGemm& g, bool streamed, hipStream_t s) {
+  if (streamed)
     launch_skinny<false, 4, 1, 4>(g, s);
   else if (tiled4_fits(g, false))
     launch_tiled4(g, false, s);

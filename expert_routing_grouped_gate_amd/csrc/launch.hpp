@@ -80,10 +80,10 @@ struct GroupedGemm {
   void* xg_out;
 };
 
-int launch_ffn_up_bf16(const GroupedGemm& g, bool small_m, hipStream_t s);
-int launch_ffn_down_bf16(const GroupedGemm& g, bool small_m, hipStream_t s);
-int launch_ffn_up_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s);
-int launch_ffn_down_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s);
+int launch_ffn_up_bf16(const GroupedGemm& g, bool streamed, hipStream_t s);
+int launch_ffn_down_bf16(const GroupedGemm& g, bool streamed, hipStream_t s);
+int launch_ffn_up_w4a8(const GroupedGemm& g, bool streamed, hipStream_t s);
+int launch_ffn_down_w4a8(const GroupedGemm& g, bool streamed, hipStream_t s);
 // LDS-tiled W4A8 GEMMs (128 x 256 block tiles) and the shapes they take.
 bool mx_tiled_fits(const GroupedGemm& g, bool swiglu);
 void launch_mx_tiled(const GroupedGemm& g, bool swiglu, hipStream_t s);

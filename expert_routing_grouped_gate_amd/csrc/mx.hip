@@ -383,10 +383,10 @@ static void launch_mx_stream(const GroupedGemm& g, hipStream_t s) {
 }
 
 // K = H (a multiple of 256): batches of 2 K-steps.  Many rows per expert
-// (small_m false) and whole tiles: the LDS-tiled kernel (mx_tiled.hip).
-int launch_ffn_up_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s) {
+// (not streamed) and whole tiles: the LDS-tiled kernel (mx_tiled.hip).
+int launch_ffn_up_w4a8(const GroupedGemm& g, bool streamed, hipStream_t s) {
   if (!mx_matrix_fits(g, true)) return -3;  // MOE_ERR_UNSUPPORTED
-  if (!small_m && mx_tiled_fits(g, true))
+  if (!streamed && mx_tiled_fits(g, true))
     launch_mx_tiled(g, true, s);
   else if ((g.K / 128) % 2 == 0)
     launch_mx_stream<true, 2>(g, s);
@@ -401,9 +401,9 @@ int launch_ffn_up_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s) {
 // 148 registers, three waves per SIMD); otherwise two batches (120
 // registers, four waves per SIMD).  Many rows per expert and K a multiple of
 // 512: the LDS-tiled kernel.
-int launch_ffn_down_w4a8(const GroupedGemm& g, bool small_m, hipStream_t s) {
+int launch_ffn_down_w4a8(const GroupedGemm& g, bool streamed, hipStream_t s) {
   if (!mx_matrix_fits(g, false)) return -3;  // MOE_ERR_UNSUPPORTED
-  if (!small_m && mx_tiled_fits(g, false))
+  if (!streamed && mx_tiled_fits(g, false))
     launch_mx_tiled(g, false, s);
   else if ((g.K / 128) % 3 == 0)
     launch_mx_stream<false, 1, 3>(g, s);

@@ -88,11 +88,15 @@ CONFIGS = {
                                       fmt="w4a8", family_seed=1005, x_seed=6),
 }
 
-# Mid-size token counts of the Qwen3-style layer (same weights), around the
-# switch from the weight-streaming GEMMs (at most 16 rows per expert on
-# average: T * k <= 16 * E, i.e. T <= 256 here) to the LDS-tiled ones.
+# Mid-size token counts of the Qwen3-style layers (same weights as the
+# decode layers), across the switch from the weight-streaming GEMMs to the
+# LDS-tiled ones (bf16: above 3 rows per expert on average, T > 48 here;
+# W4A8: above 8, T > 128).
 for _T in (64, 128, 256, 320, 512, 1024):
     CONFIGS[f"qwen3_T{_T}"] = CONFIGS["qwen3_decode"].with_(name=f"qwen3_T{_T}", T=_T, x_seed=100 + _T)
+for _T in (64, 128, 256, 512, 1024):
+    CONFIGS[f"qwen3_w4a8_T{_T}"] = CONFIGS["qwen3_decode_w4a8"].with_(name=f"qwen3_w4a8_T{_T}", T=_T,
+                                                                      x_seed=200 + _T)
 
 
 def _seed(*parts: int) -> int:

@@ -269,7 +269,11 @@ typedef struct {
  *   act      [T*k, I] in sorted-row order (output): bf16 a = SiLU(g) * u
  *            rounded to bf16; W4A8: MXFP8 codes of a with act_scales
  *            [T*k, I/32].
- * Rows r >= offsets[E] are not written. */
+ * Rows r >= offsets[E] are not written.  Kernels: weight-streaming 16-row
+ * tiles with at most 16 tokens, or with at most 3 (bf16) / 8 (W4A8) rows per
+ * expert on average when no bf16 shared expert with shared_I == I is
+ * attached; LDS-tiled 128-row tiles otherwise (the same choice in every
+ * entry point, so their outputs agree bit for bit). */
 int moe_grouped_ffn_up(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales,
                        int T, int k, const int32_t* sorted_pair, const int32_t* offsets,
                        void* act, uint8_t* act_scales, void* stream);
@@ -288,9 +292,9 @@ int moe_shared_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scale
 
 /* moe_grouped_ffn_up followed by moe_grouped_ffn_down (and moe_shared_ffn
  * when w->shared_I > 0 and shared_y is not NULL).  With bf16 weights,
- * shared_I == I and many rows per expert (T * k > 16 * E), the shared expert
- * runs as one more group inside the two routed launches; every output equals
- * the separate calls' bit for bit. */
+ * shared_I == I and more than 16 tokens, the shared expert runs as one more
+ * group inside the two routed launches; every output equals the separate
+ * calls' bit for bit. */
 int moe_grouped_ffn(const MoeFfnWeights* w, const void* x, const uint8_t* x_scales,
                     int T, int k, const int32_t* sorted_pair, const int32_t* offsets,
                     void* act, uint8_t* act_scales, uint16_t* y,

@@ -53,7 +53,7 @@ def test_hy3_adds_the_shared_expert_and_bias():
     assert w["g1_bytes"] == (155 * 25_165_824 + 4096 * 4096 * 2 + 4096 * 8 * 1536 * 2
                              + 25_165_824 + 4096 * 1536 * 2)
     assert w["g1_flops"] == 824_633_720_832 + 2 * 4096 * 2 * 1536 * 4096
-    # not folded: decode-sized rows per expert, or no shared expert
+    # not folded: at most 16 tokens (streaming GEMMs), or no shared expert
     assert not bench.workload_bytes_flops(W.CONFIGS["hy3"].with_(T=16), counts_touching(192, 80))["g1_shared"]
     assert not bench.workload_bytes_flops(W.CONFIGS["qwen3_prefill"], counts_touching(128, 128))["g1_shared"]
 
@@ -76,20 +76,29 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_gemm1_traffic_is_keyed_to_the_config_and_its_sources(tmp_path, monkeypatch):
-    assert bench.gemm1_family(W.CONFIGS["hy3"]) == "bf16_prefill"
-    assert bench.gemm1_family(W.CONFIGS["qwen3_decode"]) == "bf16_decode"
-    assert bench.gemm1_family(W.CONFIGS["qwen3_decode_w4a8"]) == "w4a8_decode"
-    assert bench.gemm1_family(W.CONFIGS["qwen3_prefill_w4a8"]) == "w4a8_prefill"
+    assert bench.gemm1_family(W.CONFIGS["hy3"]) == "bf16_tiled"
+    assert bench.gemm1_family(W.CONFIGS["qwen3_decode"]) == "bf16_stream"
+    assert bench.gemm1_family(W.CONFIGS["qwen3_decode_w4a8"]) == "w4a8_stream"
+    assert bench.gemm1_family(W.CONFIGS["qwen3_prefill_w4a8"]) == "w4a8_tiled"
+    # the library's switch: bf16 above 3 rows per expert (T > 48 at E = 128,
+    # top-8), W4A8 above 8 (T > 128), bf16 with a foldable shared expert above
+    # 16 tokens
+    assert bench.gemm1_family(W.CONFIGS["qwen3_decode"].with_(T=48)) == "bf16_stream"
+    assert bench.gemm1_family(W.CONFIGS["qwen3_decode"].with_(T=56)) == "bf16_tiled"
+    assert bench.gemm1_family(W.CONFIGS["qwen3_decode_w4a8"].with_(T=128)) == "w4a8_stream"
+    assert bench.gemm1_family(W.CONFIGS["qwen3_decode_w4a8"].with_(T=136)) == "w4a8_tiled"
+    assert bench.gemm1_family(W.CONFIGS["hy3"].with_(T=16)) == "bf16_stream"
+    assert bench.gemm1_family(W.CONFIGS["hy3"].with_(T=17)) == "bf16_tiled"
     cfg = W.CONFIGS["hy3"]
     md = tmp_path / "hbm_counters_hy3.md"
     monkeypatch.setattr(bench, "counters_md", lambda name: str(tmp_path / f"hbm_counters_{name}.md"))
     assert bench.measured_gemm1_traffic(cfg) is None                     # no summary
-    h = bench.gemm1_source_hash("bf16_prefill")
+    h = bench.gemm1_source_hash("bf16_tiled")
     md.write_text(f"gemm1_source_sha256_16: {h}\ngemm1_read_bytes: 1000\ngemm1_write_bytes: 24\n")
     assert bench.measured_gemm1_traffic(cfg) == 1024
     md.write_text("gemm1_source_sha256_16: 0000000000000000\ngemm1_read_bytes: 1000\ngemm1_write_bytes: 24\n")
     assert bench.measured_gemm1_traffic(cfg) is None                     # taken on other sources
-    assert h != bench.gemm1_source_hash("bf16_decode")
+    assert h != bench.gemm1_source_hash("bf16_stream")
 
 
 def test_host_cpu_model_is_named():

@@ -49,6 +49,11 @@ SMALL = {
     # and the next tile's first two batches are used
     "mx_d3_stream": CFG["qwen3_decode_w4a8"].with_(name="mx_d3_stream", T=1024, H=2048, E=8, k=4,
                                                    I=768, family_seed=1113, x_seed=30),
+    # 8 rows per expert on average (the streaming kernels although the tiled
+    # ones would fit), the Zipf router bias putting most tokens on the first
+    # experts: several 16-row tiles per group
+    "mx_skew_stream": CFG["qwen3_decode_w4a8"].with_(name="mx_skew_stream", T=64, H=1024, E=16, k=2,
+                                                     I=256, family_seed=1114, x_seed=31),
 }
 
 # The GEMM-level configs again with block scales spread over 2^-27 .. 2^13
@@ -287,6 +292,19 @@ def test_mx_layer_full_prefill():
     _layer_check(CFG["qwen3_prefill_w4a8"], tokens=[0, 1, 2, 777, 2048, 4094, 4095])
 
 
+# full-size W4A8 decode weights on both sides of the switch from the
+# streaming GEMMs (at most 8 rows per expert on average: T <= 128 at E = 128,
+# k = 8) to the tiled ones; values on a sample of tokens
+MID = {"qwen3_w4a8_T128": CFG["qwen3_w4a8_T128"],
+       "qwen3_w4a8_T136": CFG["qwen3_w4a8_T128"].with_(name="qwen3_w4a8_T136", T=136, x_seed=336)}
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_mx_layer_mid_size(name):
+    T = MID[name].T
+    _layer_check(MID[name], tokens=[0, 1, 2, 3, 40, 63, 64, 100, T - 3, T - 2, T - 1])
+
+
 def test_mx_full_size_expert_rows():
     """The full W4A8 prefill layer: whole experts' GEMM1 act codes (against
     the oracle's SwiGLU of the dequantised x, quantised) and GEMM2 rows (on
@@ -320,16 +338,16 @@ def test_mx_full_size_expert_rows():
 def test_mx_tiled_equals_streaming_bit_for_bit(name):
     """A row's GEMM outputs depend only on that row, and both GEMM kernels
     run the same scaled MFMAs over the same K-steps in the same order.  With
-    the routing of all T tokens, the first 16*E/k tokens alone (16 rows per
-    expert: streaming kernels) and all T tokens (tiled kernels) give the same
-    bits in every row of those tokens, in both GEMMs."""
+    the routing of all T tokens, the first 8*E/k tokens alone (8 rows per
+    expert on average: streaming kernels) and all T tokens (tiled kernels)
+    give the same bits in every row of those tokens, in both GEMMs."""
     L = get_layer(SMALL[name])
     cfg = L.cfg
     x = L.dev["x"]
     xq, xs = B.mx_quantize(x)
     logits = B.router_logits(x, L.dev["wr"])
     ids, _ = B.gate_topk(logits, cfg.k, L.mode, L.dev["bias"], cfg.routed_scale, cfg.eps)
-    nfew = 16 * cfg.E // cfg.k
+    nfew = 8 * cfg.E // cfg.k
     outs = []
     for T in (nfew, cfg.T):
         _, offsets, sp, pp = B.route(ids[:T].contiguous(), cfg.E)

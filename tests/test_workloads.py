@@ -63,3 +63,8 @@ def test_mid_size_configs_share_the_decode_weights():
         c = W.CONFIGS[f"qwen3_T{T}"]
         assert c.T == T and c.family_seed == W.CONFIGS["qwen3_decode"].family_seed
         assert (c.H, c.E, c.k, c.I) == (4096, 128, 8, 1536)
+    for T in (64, 128, 256, 512, 1024):
+        c = W.CONFIGS[f"qwen3_w4a8_T{T}"]
+        d = W.CONFIGS["qwen3_decode_w4a8"]
+        assert c.T == T and (c.family_seed, c.fmt, c.bias) == (d.family_seed, d.fmt, d.bias)
+        assert (c.H, c.E, c.k, c.I) == (4096, 128, 8, 1536)
