@@ -58,8 +58,9 @@ def parse():
     return ap.parse_args()
 
 
-# GEMM1 (w13 + SwiGLU) of each layer config: the sources its kernel is built
-# from and the kernel-name prefix rocprofv3 reports.  A counter summary
+# The kernel each bench config grades (layers: GEMM1, w13 + SwiGLU; the norm
+# configs: their one kernel): the sources it is built from and the
+# kernel-name prefix rocprofv3 reports.  A counter summary
 # (profiles/hbm_counters_<config>.md) records the hash of those sources; its
 # byte counts are reported as roofline.traffic only while the hash matches.
 _CSRC = "expert_routing_grouped_gate_amd/csrc/"
@@ -68,6 +69,12 @@ GEMM1 = {
     "bf16_tiled": ((_CSRC + "tiled_bf16.hip", _CSRC + "common.hpp", _CSRC + "mxfmt.hpp"), "ffn_tiled4<true"),
     "w4a8_stream": ((_CSRC + "mx.hip", _CSRC + "common.hpp", _CSRC + "mxfmt.hpp"), "ffn_mx_stream<true"),
     "w4a8_tiled": ((_CSRC + "mx_tiled.hip", _CSRC + "common.hpp", _CSRC + "mxfmt.hpp"), "ffn_mx_tiled<true"),
+}
+_NORM_SRC = (_CSRC + "norm.hip", _CSRC + "rowops.hpp", _CSRC + "common.hpp", _CSRC + "mxfmt.hpp")
+NORM_KERNELS = {
+    "add_rmsnorm": (_NORM_SRC, "add_rmsnorm_kernel"),
+    "add_rmsnorm_mx": (_NORM_SRC, "add_rmsnorm_kernel"),
+    "combine_add_rmsnorm": (_NORM_SRC, "combine_add_rmsnorm_kernel"),
 }
 
 
@@ -137,13 +144,24 @@ class TimingEvent:
             TimingEvent._hip.hipEventDestroy(self.cuda_event)
 
 
-def gemm1_source_hash(family: str) -> str:
+def graded_kernel(config: str):
+    """(sources, rocprofv3 kernel-name prefix) of the kernel a bench config grades."""
+    if config in NORM_KERNELS:
+        return NORM_KERNELS[config]
+    return GEMM1[gemm1_family(_layer_configs()[config])]
+
+
+def source_hash(sources) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in GEMM1[family][0]:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def gemm1_source_hash(family: str) -> str:
+    return source_hash(GEMM1[family][0])
 
 
 def _counter_means(path):
@@ -189,23 +207,21 @@ def summarize_counters(config, fetch_csv, write_csv, copy_fetch_csv, copy_write_
              "| kernel | FETCH_SIZE KiB | read bytes (scaled) | WRITE_SIZE KiB | written bytes (scaled) |",
              "|---|---|---|---|---|"]
     g1 = None
-    family = None
-    if config in _layer_configs():
-        family = gemm1_family(_layer_configs()[config])
+    graded = graded_kernel(config) if (config in NORM_KERNELS or config in _layer_configs()) else None
     for k in sorted(fetch, key=lambda k: -fetch[k]):
         if not k.startswith(("void moe::", "moe::")):
             continue
         rb, wb = fetch[k] * sf * 1024, write.get(k, 0.0) * sw * 1024
         lines.append(f"| `{k[:80]}` | {fetch[k]:,.1f} | {rb / 1e9:.4f} GB | {write.get(k, 0.0):,.1f} | {wb / 1e6:.3f} MB |")
-        if family is not None and GEMM1[family][1] in k and g1 is None:
+        if graded is not None and graded[1] in k.split("(")[0] and g1 is None:
             g1 = (rb, wb)
-    if family is not None:
-        lines += ["", "Machine-readable (bench.py reports `roofline.traffic` from these only while the GEMM1 "
-                  "sources still hash to the value below):", "",
-                  f"gemm1_kernel: {GEMM1[family][1]}",
-                  f"gemm1_source_sha256_16: {gemm1_source_hash(family)}",
-                  f"gemm1_read_bytes: {int(g1[0]) if g1 else 0}",
-                  f"gemm1_write_bytes: {int(g1[1]) if g1 else 0}"]
+    if graded is not None:
+        lines += ["", "Machine-readable (bench.py reports `roofline.traffic` from these only while the graded "
+                  "kernel's sources still hash to the value below):", "",
+                  f"kernel: {graded[1]}",
+                  f"kernel_source_sha256_16: {source_hash(graded[0])}",
+                  f"kernel_read_bytes: {int(g1[0]) if g1 else 0}",
+                  f"kernel_write_bytes: {int(g1[1]) if g1 else 0}"]
     lines.append("")
     print("\n".join(lines))
 
@@ -215,22 +231,26 @@ def _layer_configs():
     return W.CONFIGS
 
 
-def measured_gemm1_traffic(cfg):
-    """HBM bytes per GEMM1 launch from the committed counter summary of this
-    config, or None when it is missing or was taken on other GEMM1 sources."""
-    family = gemm1_family(cfg)
+def measured_traffic(config: str):
+    """HBM bytes per launch of the graded kernel from the committed counter
+    summary of this config, or None when it is missing or was taken on other
+    sources of that kernel."""
     try:
         kv = {}
-        for line in open(counters_md(cfg.name)):
-            if ":" in line and line.split(":")[0].strip() in ("gemm1_source_sha256_16", "gemm1_read_bytes",
-                                                              "gemm1_write_bytes"):
+        for line in open(counters_md(config)):
+            if ":" in line and line.split(":")[0].strip() in ("kernel_source_sha256_16", "kernel_read_bytes",
+                                                              "kernel_write_bytes"):
                 a, b = line.split(":", 1)
                 kv[a.strip()] = b.strip()
-        if kv.get("gemm1_source_sha256_16") != gemm1_source_hash(family):
+        if kv.get("kernel_source_sha256_16") != source_hash(graded_kernel(config)[0]):
             return None
-        return int(kv["gemm1_read_bytes"]) + int(kv["gemm1_write_bytes"])
+        return int(kv["kernel_read_bytes"]) + int(kv["kernel_write_bytes"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def measured_gemm1_traffic(cfg):
+    return measured_traffic(cfg.name)
 
 
 def host_cpu_model() -> str:
@@ -385,7 +405,7 @@ def bench_combine_norm(args):
                                "the next residual add + RMSNorm (fp32 + bf16 outputs, bf16 residual)",
                    "T": T, "k": k, "H": H, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config),
                      "kernel": "combine_add_rmsnorm_kernel", "kernel_ms": round(k_ms, 5), "algorithmic_bytes": alg},
         "separate": {"ms_per_step": round(sep_ms, 5), "events_ms": round(sep_k_ms, 5),
                      "calls": "moe_combine + moe_add_rmsnorm"},
@@ -450,7 +470,7 @@ def bench_norm(args):
         "config": {"workload": f"{args.config}: residual add + RMSNorm before the MoE layer, T={T} H={H}, {form}",
                    "T": T, "H": H, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "add_rmsnorm_kernel",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.config), "kernel": "add_rmsnorm_kernel",
                      "kernel_ms": round(k_ms, 5), "algorithmic_bytes": alg},
         "cpu_baseline": cpu_b,
     }

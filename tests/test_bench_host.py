@@ -94,11 +94,17 @@ def test_gemm1_traffic_is_keyed_to_the_config_and_its_sources(tmp_path, monkeypa
     monkeypatch.setattr(bench, "counters_md", lambda name: str(tmp_path / f"hbm_counters_{name}.md"))
     assert bench.measured_gemm1_traffic(cfg) is None                     # no summary
     h = bench.gemm1_source_hash("bf16_tiled")
-    md.write_text(f"gemm1_source_sha256_16: {h}\ngemm1_read_bytes: 1000\ngemm1_write_bytes: 24\n")
+    md.write_text(f"kernel_source_sha256_16: {h}\nkernel_read_bytes: 1000\nkernel_write_bytes: 24\n")
     assert bench.measured_gemm1_traffic(cfg) == 1024
-    md.write_text("gemm1_source_sha256_16: 0000000000000000\ngemm1_read_bytes: 1000\ngemm1_write_bytes: 24\n")
+    md.write_text("kernel_source_sha256_16: 0000000000000000\nkernel_read_bytes: 1000\nkernel_write_bytes: 24\n")
     assert bench.measured_gemm1_traffic(cfg) is None                     # taken on other sources
     assert h != bench.gemm1_source_hash("bf16_stream")
+    # the norm configs grade their one kernel, keyed to the norm sources
+    assert bench.graded_kernel("combine_add_rmsnorm")[1] == "combine_add_rmsnorm_kernel"
+    hn = bench.source_hash(bench.graded_kernel("add_rmsnorm")[0])
+    (tmp_path / "hbm_counters_add_rmsnorm.md").write_text(
+        f"kernel_source_sha256_16: {hn}\nkernel_read_bytes: 7\nkernel_write_bytes: 3\n")
+    assert bench.measured_traffic("add_rmsnorm") == 10
 
 
 def test_host_cpu_model_is_named():
