@@ -11,6 +11,13 @@
 // sub-round, ranked inside a wave by matching the 8 id bits with ballots and
 // across the block's 4 waves through per-wave counts in LDS.  No atomics
 // touch global memory, so the result is deterministic.
+//
+// Up to RDIRECT chunks every scatter block sums the histograms it needs
+// itself (chunks x (E+1) loads per block, no extra launch).  Beyond that a
+// scan kernel first replaces each expert's column of chunk counts by its
+// exclusive prefix over the chunks, in place, and writes the totals to one
+// more row, so that each scatter block reads two rows: the work stays
+// linear in the number of chunks instead of quadratic.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -18,12 +25,13 @@ namespace moe {
 
 constexpr int RCHUNK = 1024;
 constexpr int RSUB = RCHUNK / 256;
+constexpr int RDIRECT = 64;
 
 size_t route_workspace_bytes(int T, int k, int E) {
   const long long R = (long long)T * k;
   const long long nb = (R + RCHUNK - 1) / RCHUNK;
   if (nb <= 1) return 0;
-  return (size_t)nb * (size_t)(E + 1) * sizeof(int32_t);
+  return (size_t)(nb + (nb > RDIRECT ? 1 : 0)) * (size_t)(E + 1) * sizeof(int32_t);
 }
 
 __global__ __launch_bounds__(256) void route_hist(const int32_t* __restrict__ ids, int R, int E,
@@ -40,6 +48,34 @@ __global__ __launch_bounds__(256) void route_hist(const int32_t* __restrict__ id
   }
   __syncthreads();
   for (int i = tid; i <= E; i += 256) ws[(size_t)blockIdx.x * (E + 1) + i] = h[i];
+}
+
+// Column i (expert i, or E for the dropped pairs) of the chunk histograms:
+// ws[c][i] becomes the count of i in chunks before c, ws[nb][i] the total.
+// One block per column; thread t sums a contiguous run of chunks, a block
+// scan gives each run its base, and the run is rewritten in order.
+__global__ __launch_bounds__(256) void route_scan(int nb, int E, int32_t* __restrict__ ws) {
+  __shared__ int wsum[4];
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t stride = (size_t)(E + 1);
+  const int per = (nb + 255) / 256;
+  const int c0 = min(nb, tid * per), c1 = min(nb, c0 + per);
+  int sum = 0;
+  for (int c = c0; c < c1; ++c) sum += ws[(size_t)c * stride + i];
+  const int incl = wave_incl_scan(sum);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int run = before + incl - sum;
+  for (int c = c0; c < c1; ++c) {
+    const size_t at = (size_t)c * stride + i;
+    const int v = ws[at];
+    ws[at] = run;
+    run += v;
+  }
+  if (tid == 255) ws[(size_t)nb * stride + i] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
 __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__ ids, int R,
@@ -80,6 +116,12 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
       }
     }
     for (int i = tid; i < E; i += 256) run[i] = 0;
+  } else if (nb > RDIRECT) {
+    // prefixes and totals from route_scan
+    for (int i = tid; i <= E; i += 256) {
+      tot[i] = ws[(size_t)nb * (E + 1) + i];
+      if (i < E) run[i] = ws[(size_t)b * (E + 1) + i];
+    }
   } else {
     for (int i = tid; i <= E; i += 256) {
       int sum = 0, pre = 0;
@@ -154,6 +196,7 @@ int launch_route(const int32_t* ids, int T, int k, int E, int32_t* counts, int32
   const int R = T * k;
   const int nb = (R + RCHUNK - 1) / RCHUNK;
   if (nb > 1) hipLaunchKernelGGL(route_hist, dim3(nb), dim3(256), 0, s, ids, R, E, ws);
+  if (nb > RDIRECT) hipLaunchKernelGGL(route_scan, dim3(E + 1), dim3(256), 0, s, nb, E, ws);
   hipLaunchKernelGGL(route_scatter, dim3(nb), dim3(256), 0, s, ids, R, E, nb, ws, counts, offsets,
                      sorted_pair, pair_pos, dev_status);
   return launch_status();

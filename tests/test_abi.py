@@ -90,6 +90,10 @@ def test_gate_topk_checks(lib):
 def test_route_checks_and_workspace(lib):
     assert lib.moe_route_workspace_size(16, 8, 128) == 0           # one chunk
     assert lib.moe_route_workspace_size(4096, 8, 192) == 32 * 193 * 4   # 1024-pair chunks
+    assert lib.moe_route_workspace_size(8192, 8, 128) == 64 * 129 * 4   # the last direct count
+    # more than 64 chunks: one more row for the per-expert totals of the chunk scan
+    assert lib.moe_route_workspace_size(8193, 8, 128) == (65 + 1) * 129 * 4
+    assert lib.moe_route_workspace_size(40000, 16, 256) == (625 + 1) * 257 * 4
     f = lib.moe_route
     assert f(FAKE, 4096, 8, 192, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == WS
     assert f(FAKE, 4096, 8, 192, FAKE, FAKE, FAKE, FAKE, None, FAKE, 100, None) == WS

@@ -134,8 +134,12 @@ def _distinct_ids(T, E, k, seed):
     return torch.stack([torch.randperm(E, generator=g)[:k] for _ in range(T)]).to(torch.int32)
 
 
+# (8192, 128, 8) is 64 chunks of 1024 pairs, the last count whose bases each
+# scatter block sums itself; (8193, 128, 8) the first that scans the chunk
+# histograms first; (40000, 256, 16) 625 chunks
 @pytest.mark.parametrize("T,E,k", [(16, 128, 8), (300, 128, 8), (4096, 192, 8), (1, 1, 1),
-                                   (5000, 256, 1), (2049, 3, 1), (256, 8, 8), (513, 256, 32)])
+                                   (5000, 256, 1), (2049, 3, 1), (256, 8, 8), (513, 256, 32),
+                                   (8192, 128, 8), (8193, 128, 8), (40000, 256, 16)])
 def test_route_bit_exact(T, E, k):
     ids = _distinct_ids(T, E, k, T + E + k)
     st = torch.full((4,), 77, dtype=torch.int32, device="cuda")
