@@ -73,7 +73,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   // One LDS array, the ring (a second __shared__ variable makes the compiler
   // wait for every outstanding DMA before each LDS read); the scheduler's
   // table stays in registers.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::NS * C::STAGE + (SWIGLU ? 0 : C::NW * 2048)];
   TileMap tm;
   tm.init(g.offsets, g.G, g.ident_rows, C::BM, g.total_rows, g.xg_rows);
   const int total = __builtin_amdgcn_readfirstlane(tm.total * n_tiles);
@@ -83,7 +83,9 @@ __global__ __launch_bounds__(512, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % C::WM, wn = wave / C::WM;
+  // waves w and w + 4 share a SIMD: they take the two row halves of the
+  // same 64 columns, so a half of padding rows idles one wave per SIMD
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int li = lane & 15, kc = lane >> 4;
   const int K = g.K, nk = K / 64;  // nk >= 5 (launcher)
   const uint32_t rowb = 2u * (uint32_t)K;  // bytes per row
@@ -213,7 +215,21 @@ __global__ __launch_bounds__(512, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
   // DMA loads (LPW per wave and step, one step's worth issued after the
   // target on every path); other loads and stores in between only make it
   // stricter.
+  //
+  // A wave whose 64 rows of the current tile are all padding (an expert's
+  // last, partial m-tile) skips the MFMAs and the second-half reads: it keeps
+  // its share of the DMA, the waits and the barrier, and reads the next first
+  // half like every wave, so both kinds of step leave the same state behind.
+  bool act = true;  // this wave's 64 rows hold valid rows of the current tile
   auto step = [&](f32x4 (&acc)[MT][NT], const T4Tile& ti, const uint32_t* adma, int st) {
+    if (!act) {
+      wait_vm<C::LPW>();
+      block_barrier();
+      issue(ti, adma, buf, st);
+      buf = buf == C::NS - 1 ? 0 : buf + 1;
+      read_half(f0, buf, 0);
+      return;
+    }
     read_half(f1, buf, 1);
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
@@ -263,6 +279,7 @@ __global__ __launch_bounds__(512, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
     const bool has_next = tn < total;
     if (has_next) nxt = locate(tn);
     gather_issue(nxt, nxt_raw);  // (the current tile again when there is no next)
+    act = __builtin_amdgcn_readfirstlane(64 * wm < cur.nrows ? 1 : 0) != 0;
     f32x4 acc[MT][NT];  // (scoped to the tile: no accumulator value crosses tiles)
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi)
@@ -300,6 +317,8 @@ __global__ __launch_bounds__(512, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
     constexpr int NG = SWIGLU ? NT / 2 : NT;  // output groups per wave
     const int odd = kc & 1;
     const int col = (SWIGLU ? C::BN / 2 : C::BN) / C::WN * wn + 8 * (kc >> 1);
+    // GEMM2: this wave's 2 KB of LDS past the ring, for the row-slice stores
+    uint8_t* const oscr = smem + C::NS * C::STAGE + wave * 2048;
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
       const int r = 64 * wm + 16 * mi + li;
@@ -327,7 +346,26 @@ __global__ __launch_bounds__(512, 1) void ffn_tiled4(GroupedGemm g, int n_tiles)
         } else {
           o = u32x4{pk[0].x, pk[0].y, s0[1], s1[1]};  // group np, columns 8 (kc>>1) ..
         }
-        if (r < cur.nrows) *reinterpret_cast<u32x4*>(orow + 16 * (np + odd)) = o;
+        if (SWIGLU) {
+          if (r < cur.nrows) *reinterpret_cast<u32x4*>(orow + 16 * (np + odd)) = o;
+        } else {
+          // 16-byte chunk 2 (np + odd) + (kc >> 1) of row li of the wave's
+          // 128-byte row slices, XOR-swizzled by the row
+          *reinterpret_cast<u32x4*>(oscr + li * 128 + 16 * ((2 * (np + odd) + (kc >> 1)) ^ (li & 7))) = o;
+        }
+      }
+      if (!SWIGLU) {
+        // the wave's 16 rows x 64 columns back from LDS as whole 128-byte
+        // row slices: lane l takes chunk l % 8 of row l / 8 (+ 8), so one
+        // store covers 8 full rows instead of 16 half rows
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int rr = 8 * j + (lane >> 3), c = lane & 7;
+          const u32x4 o = *reinterpret_cast<const u32x4*>(oscr + rr * 128 + 16 * (c ^ (rr & 7)));
+          const int rg = 64 * wm + 16 * mi + rr;
+          if (rg < cur.nrows)
+            *reinterpret_cast<u32x4*>(out + (size_t)(orow0 + rg) * g.N + cur.n0 + C::BN / C::WN * wn + 8 * c) = o;
+        }
       }
     }
     if (!has_next) {
