@@ -29,6 +29,18 @@
 // tile DMA the next tile's first three, so the stream never drains between
 // tiles.  Fragments are read from LDS a half-step (K = 32) ahead of the
 // MFMAs that use them.
+//
+// Both operands depend on L2 reuse: an expert's m-tiles share each weight
+// slab and its n-tiles each activation tile, and the blocks of one XCD run
+// neighbouring tiles at once.  Marking either operand's copies non-temporal
+// made the kernel 26-35% slower; with half of the weight lines hitting L2 (a
+// timing probe) it ran 15% faster, so the weight lines fetched from beyond
+// L2 are what the stream waits for.
+//
+// Epilogue: SwiGLU (GEMM1) and bf16 stores from registers.  GEMM1 stores each
+// lane's 8 columns directly (a wave holds 32 output columns: 64-byte row
+// slices); GEMM2 passes each wave's 16 x 64 results through 2 KB of LDS past
+// the ring so that one store writes 8 whole 128-byte row slices.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mxfmt.hpp"
