@@ -52,18 +52,31 @@ namespace {
 
 using moe::GroupedGemm;
 
-// Device address of `scratch` on the current GPU, or nullptr when the runtime
-// cannot give it.  Looked up once per device (hipGetSymbolAddress with that
-// device current) and kept.
-void* scratch_device_ptr() {
+// Device address of `scratch` on the GPU that `stream` runs on (the current
+// GPU for the null stream), or nullptr when the runtime cannot give it.
+// Looked up once per device, with that device current (switched to and back
+// when it is not), and kept.
+void* scratch_device_ptr(hipStream_t stream) {
   static std::mutex mu;
   static void* ptrs[64] = {};
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (stream != nullptr) {
+    hipDevice_t d = -1;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return nullptr;
+    dev = d;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return nullptr;
+  }
+  if (dev < 0 || dev >= 64) return nullptr;
   std::lock_guard<std::mutex> lock(mu);
   if (ptrs[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+    if (e != hipSuccess || p == nullptr) return nullptr;
     ptrs[dev] = p;
   }
   return ptrs[dev];
@@ -612,7 +625,7 @@ int moe_layer_forward_noalloc(const MoeLayerDesc* d, const uint16_t* x, int T, u
   s.workspace_bytes = 0;
   if (T > 0) {
     // moe_layer_forward validates everything else before it enqueues
-    void* p = scratch_device_ptr();
+    void* p = scratch_device_ptr(as_stream(stream));
     if (p == nullptr) return MOE_ERR_LAUNCH;
     s.workspace = p;
     s.workspace_bytes = MOE_NOALLOC_SCRATCH_BYTES;

@@ -380,8 +380,9 @@ int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t*
  * use on that GPU until the process ends.  The call allocates nothing.
  *   Limit: moe_layer_workspace_size(d, T) <= MOE_NOALLOC_SCRATCH_BYTES (the
  *   router part never exceeds 64 MiB; the routing part does only beyond
- *   about 60 million routed pairs at E = 256), else MOE_ERR_SCRATCH and
- *   nothing is enqueued.
+ *   about 66 million routed pairs at E = 256), else MOE_ERR_SCRATCH and
+ *   nothing is enqueued.  The array used is the one of the GPU that `stream`
+ *   runs on (the current GPU for the null stream).
  *   Every call on one GPU shares that GPU's array, which keeps the last
  *   call's contents (every byte a call reads from it, that call wrote
  *   first, so nothing needs to start at zero).  Calls that overlap on one
