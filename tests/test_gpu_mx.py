@@ -28,7 +28,7 @@ SMALL = {
     # Hy3-style gate with an always-on W4A8 shared expert
     "mx_shared": CFG["hy3"].with_(name="mx_shared", T=40, H=512, E=16, k=4, I=256, shared_I=384,
                                   fmt="w4a8", family_seed=1108, x_seed=25),
-    # more than 16 rows per expert and K a multiple of 512, at least 1024:
+    # more than 8 rows per expert on average and K a multiple of 512, at least 1024:
     # the LDS-tiled kernels; two quads of K-steps per tile ...
     "mx_tiled": CFG["qwen3_decode_w4a8"].with_(name="mx_tiled", T=512, H=1024, E=8, k=2, I=1024,
                                                family_seed=1109, x_seed=26),

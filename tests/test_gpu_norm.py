@@ -270,7 +270,7 @@ def _separate(y, pp, w, shared, weight, eps, res):
 
 @pytest.mark.parametrize("with_shared,with_residual", [(True, True), (False, True), (False, False)])
 def test_combine_add_rmsnorm_equals_separate_calls_on_a_layer(with_shared, with_residual):
-    """The expert rows of a real layer (the one-wave-per-SIMD tiled path,
+    """The expert rows of a real layer (the LDS-tiled GEMM path,
     sigmoid gating, shared expert): every output of the fused call equals
     moe_combine then moe_add_rmsnorm bit for bit; the combined rows match the
     oracle's combine of the same expert rows."""

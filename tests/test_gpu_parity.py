@@ -30,7 +30,7 @@ SMALL = {
     # decode-sized (T <= 16): the layer's two-launch routing front end
     "wide_k_decode": CFG["tiny"].with_(name="wide_k_decode", T=16, E=256, k=32, I=128, x_seed=16,
                                        family_seed=1099),
-    # many rows per expert with K >= 320: the one-wave-per-SIMD tiled GEMMs
+    # many rows per expert with K >= 320: the eight-wave LDS-tiled GEMMs
     # (GEMM1 K = 512: 8 steps; GEMM2 K = 384: 6 steps), ragged m-tiles
     "tiled4": CFG["tiny"].with_(name="tiled4", T=600, H=512, E=8, k=2, I=384, x_seed=17,
                                 family_seed=1017),
@@ -449,7 +449,7 @@ def test_one_expert_layer_is_the_plain_mlp():
 def test_all_tokens_on_one_expert(T, H, I):
     """A router bias that makes expert 3 win for every token: one group holds
     all rows, the others none (ragged extreme; the second shape runs the
-    one-wave-per-SIMD tiled kernels with 8 m-tiles in one group)."""
+    eight-wave LDS-tiled kernels with 8 m-tiles in one group)."""
     cfg = CFG["tiny"].with_(name=f"skew_{H}", T=T, H=H, I=I, E=8, k=1, x_seed=35, family_seed=1035 + H)
     L = get_layer(cfg)
     bias = torch.zeros(cfg.E)
