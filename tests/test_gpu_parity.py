@@ -355,6 +355,15 @@ def test_layer_full_size(name, tokens):
     _layer_check(CFG[name], tokens)
 
 
+def test_layer_routing_beyond_64_chunks():
+    """The Qwen3-shape layer at T = 8200: 65,600 routed pairs are 65 chunks of
+    1024, so the layer's routing scans the chunk histograms first (one more
+    workspace row); routing bit-exact on every token, values on a sample."""
+    cfg = CFG["qwen3_prefill"].with_(name="qwen3_T8200", T=8200, x_seed=8200)
+    assert B.load().moe_route_workspace_size(cfg.T, cfg.k, cfg.E) == (65 + 1) * (cfg.E + 1) * 4
+    _layer_check(cfg, [0, 1, 4099, 8198, 8199])
+
+
 def _expert_rows_check(L, b, experts):
     """act and y of whole experts of a layer call, element by element: act
     against the oracle's bf16(SiLU(x Wg^T) * (x Wu^T)) of the expert's
