@@ -360,6 +360,29 @@ def test_mx_tiled_equals_streaming_bit_for_bit(name):
         assert torch.equal(few, many), what
 
 
+@pytest.mark.parametrize("name", ["mx_shared", "mx_tiled_deep"])
+def test_mx_non_finite_token_stays_in_its_row(name):
+    """NaN in one token's hidden state (its MXFP8 blocks, logits, activations
+    and shared-expert row): the token still routes to k distinct experts in
+    range, and every other token's output equals the clean run's bit for bit
+    (each 32-block and each GEMM row is its own)."""
+    L = get_layer(SMALL[name])
+    cfg = L.cfg
+    layer = L.layer()
+    clean = layer.forward(L.dev["x"]).clone()
+    x = L.dev["x"].clone()
+    x[3, ::5] = float("nan")
+    out = layer.forward(x).clone()
+    torch.cuda.synchronize()
+    ids = np_(layer.buf["topk_ids"])
+    assert ids.min() >= 0 and ids.max() < cfg.E
+    assert all(len(set(row)) == cfg.k for row in ids)
+    assert int(np_(layer.buf["counts"]).sum()) == cfg.T * cfg.k
+    keep = torch.ones(cfg.T, dtype=torch.bool)
+    keep[3] = False
+    assert torch.equal(out[keep.cuda()], clean[keep.cuda()])
+
+
 def test_mx_layer_deterministic_and_graph_capture():
     L = get_layer(SMALL["mx_mid"])
     layer = L.layer()

@@ -320,6 +320,32 @@ def test_layer_deterministic(name):
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("name,bad", [("small_prefill", float("nan")), ("tiled4_hy3", float("nan")),
+                                      ("tiled4_hy3", float("inf")), ("tiny", float("-inf"))])
+def test_non_finite_token_stays_in_its_row(name, bad):
+    """A token whose hidden state holds NaN or infinity (so do its logits)
+    still routes to k distinct experts in range, nothing is flagged as a bad
+    id, and every other token's output is bit-equal to the clean run: rows
+    never mix in the GEMMs or the combine."""
+    L = get_layer(SMALL[name])
+    cfg = L.cfg
+    layer = L.layer()
+    clean = layer.forward(L.dev["x"]).clone()
+    x = L.dev["x"].clone()
+    t_bad = min(5, cfg.T - 1)
+    x[t_bad, ::3] = bad
+    out = layer.forward(x).clone()
+    torch.cuda.synchronize()
+    ids = to_np(layer.buf["topk_ids"])
+    assert ids.min() >= 0 and ids.max() < cfg.E
+    assert all(len(set(row)) == cfg.k for row in ids)
+    assert int(to_np(layer.buf["counts"]).sum()) == cfg.T * cfg.k
+    assert int(to_np(layer.buf["dev_status"])[0]) == 0
+    keep = torch.ones(cfg.T, dtype=torch.bool)
+    keep[t_bad] = False
+    assert torch.equal(out[keep.cuda()], clean[keep.cuda()])
+
+
 @pytest.mark.parametrize("name", ["small_prefill", "tiled4_hy3"])
 def test_layer_graph_capture_replays(name):
     L = get_layer(SMALL[name])
