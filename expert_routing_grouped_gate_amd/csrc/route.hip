@@ -5,12 +5,13 @@
 //
 // One 8-bit digit (E <= 256) means one counting-sort pass.  Pairs are cut
 // into chunks of RCHUNK; with more than one chunk a first kernel writes each
-// chunk's histogram to the workspace.  The scatter kernel turns the
-// histograms into per-expert bases (global exclusive scan + the counts of
-// earlier chunks) and places its chunk's pairs in order: 256 pairs per
-// sub-round, ranked inside a wave by matching the 8 id bits with ballots and
-// across the block's 4 waves through per-wave counts in LDS.  No atomics
-// touch global memory, so the result is deterministic.
+// chunk's histogram to the workspace.  The scatter kernel (one 1024-thread
+// block per chunk, one pair per thread) turns the histograms into
+// per-expert bases (global exclusive scan + the counts of earlier chunks)
+// and places its chunk's pairs in order in one round: ranked inside a wave
+// by matching the 8 id bits with ballots and across the block's 16 waves
+// through per-wave counts in LDS.  No atomics touch global memory, so the
+// result is deterministic.
 //
 // Up to RDIRECT chunks every scatter block sums the histograms it needs
 // itself (chunks x (E+1) loads per block, no extra launch).  Beyond that a
@@ -24,7 +25,6 @@
 namespace moe {
 
 constexpr int RCHUNK = 1024;
-constexpr int RSUB = RCHUNK / 256;
 constexpr int RDIRECT = 64;
 
 size_t route_workspace_bytes(int T, int k, int E) {
@@ -78,52 +78,39 @@ __global__ __launch_bounds__(256) void route_scan(int nb, int E, int32_t* __rest
   if (tid == 255) ws[(size_t)nb * stride + i] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
-__global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__ ids, int R,
-                                                     int E, int nb, const int32_t* __restrict__ ws,
-                                                     int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ sorted_pair,
-                                                     int32_t* __restrict__ pair_pos,
-                                                     int32_t* __restrict__ dev_status) {
+__global__ __launch_bounds__(1024) void route_scatter(const int32_t* __restrict__ ids, int R,
+                                                      int E, int nb, const int32_t* __restrict__ ws,
+                                                      int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ sorted_pair,
+                                                      int32_t* __restrict__ pair_pos,
+                                                      int32_t* __restrict__ dev_status) {
   __shared__ int tot[257];
   __shared__ int run[256];
   __shared__ int wsum[4];
-  __shared__ int wcnt[4][256];
+  __shared__ int wcnt[16][256];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
-  const int p0 = b * RCHUNK;
-  const int p1 = min(R, p0 + RCHUNK);
-
-  // this thread's ids for all sub-rounds, loaded up front
-  int myid[RSUB];
-#pragma unroll
-  for (int s = 0; s < RSUB; ++s) {
-    const int p = p0 + s * 256 + tid;
-    myid[s] = p < p1 ? ids[p] : -1;
-  }
+  const int p = b * RCHUNK + tid;  // one pair per thread
+  const bool inrange = p < R;
+  const int e = inrange ? ids[p] : -1;
+  const bool ok = inrange && e >= 0 && e < E;
 
   // 1. per-expert totals and the counts of earlier chunks
   if (nb == 1) {
-    for (int i = tid; i <= E; i += 256) tot[i] = 0;
+    for (int i = tid; i <= E; i += 1024) tot[i] = 0;
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < RSUB; ++s) {
-      const int p = p0 + s * 256 + tid;
-      if (p < p1) {
-        const int e = myid[s];
-        atomicAdd(&tot[(e >= 0 && e < E) ? e : E], 1);
-      }
-    }
-    for (int i = tid; i < E; i += 256) run[i] = 0;
+    if (inrange) atomicAdd(&tot[ok ? e : E], 1);
+    for (int i = tid; i < E; i += 1024) run[i] = 0;
   } else if (nb > RDIRECT) {
     // prefixes and totals from route_scan
-    for (int i = tid; i <= E; i += 256) {
+    for (int i = tid; i <= E; i += 1024) {
       tot[i] = ws[(size_t)nb * (E + 1) + i];
       if (i < E) run[i] = ws[(size_t)b * (E + 1) + i];
     }
   } else {
-    for (int i = tid; i <= E; i += 256) {
+    for (int i = tid; i <= E; i += 1024) {
       int sum = 0, pre = 0;
       for (int bb = 0; bb < nb; ++bb) {
         const int v = ws[(size_t)bb * (E + 1) + i];
@@ -134,17 +121,35 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
       if (i < E) run[i] = pre;
     }
   }
+  // the rank counts of the placement below start at zero
+  for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
   __syncthreads();
 
-  // 2. exclusive scan of the totals over experts (E <= 256 = one per thread)
-  const int v = tid < E ? tot[tid] : 0;
-  const int incl = wave_incl_scan(v);
-  if (lane == 63) wsum[wave] = incl;
+  // 2. exclusive scan of the totals over experts (E <= 256 = one per thread
+  // of waves 0..3)
+  int v = 0, incl = 0;
+  if (tid < 256) {
+    v = tid < E ? tot[tid] : 0;
+    incl = wave_incl_scan(v);
+    if (lane == 63) wsum[wave] = incl;
+  }
+  // 3. stable placement of the chunk's pairs in one round: within a wave by
+  // matching the 8 id bits with ballots, across the 16 waves through
+  // per-wave counts in LDS
+  unsigned long long match = __ballot(ok);
+#pragma unroll
+  for (int bit = 0; bit < 8; ++bit) {
+    const bool on = ok && ((e >> bit) & 1);
+    const unsigned long long bb = __ballot(on);
+    match &= ((e >> bit) & 1) ? bb : ~bb;
+  }
+  const int rank = __popcll(match & ((1ull << lane) - 1ull));
+  if (ok && rank == 0) wcnt[wave][e] = __popcll(match);
   __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  const int excl = before + incl - v;
   if (tid < E) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const int excl = before + incl - v;
     run[tid] += excl;
     if (b == 0) {
       counts[tid] = v;
@@ -154,39 +159,13 @@ __global__ __launch_bounds__(256) void route_scatter(const int32_t* __restrict__
   }
   if (b == 0 && tid == 0 && dev_status != nullptr) *dev_status = tot[E] > 0 ? 1 : 0;
   __syncthreads();
-
-  // 3. stable scatter, 256 pairs per sub-round
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
-  for (int s = 0; s < RSUB; ++s) {
-    const int sbeg = p0 + s * 256;
-    if (sbeg >= p1) break;  // block-uniform
-    const int p = sbeg + tid;
-    const int e = myid[s];
-    const bool inrange = p < p1;
-    const bool ok = inrange && e >= 0 && e < E;
-    for (int i = tid; i < 4 * 256; i += 256) (&wcnt[0][0])[i] = 0;
-    __syncthreads();
-    unsigned long long match = __ballot(ok);
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool on = ok && ((e >> bit) & 1);
-      const unsigned long long bb = __ballot(on);
-      match &= ((e >> bit) & 1) ? bb : ~bb;
-    }
-    const int rank = __popcll(match & lt_mask);
-    if (ok && rank == 0) wcnt[wave][e] = __popcll(match);
-    __syncthreads();
-    if (ok) {
-      int pos = run[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-      sorted_pair[pos] = p;
-      pair_pos[p] = pos;
-    } else if (inrange) {
-      pair_pos[p] = -1;
-    }
-    __syncthreads();
-    for (int i = tid; i < E; i += 256) run[i] += wcnt[0][i] + wcnt[1][i] + wcnt[2][i] + wcnt[3][i];
-    __syncthreads();
+  if (ok) {
+    int pos = run[e] + rank;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+    sorted_pair[pos] = p;
+    pair_pos[p] = pos;
+  } else if (inrange) {
+    pair_pos[p] = -1;
   }
 }
 
@@ -197,7 +176,7 @@ int launch_route(const int32_t* ids, int T, int k, int E, int32_t* counts, int32
   const int nb = (R + RCHUNK - 1) / RCHUNK;
   if (nb > 1) hipLaunchKernelGGL(route_hist, dim3(nb), dim3(256), 0, s, ids, R, E, ws);
   if (nb > RDIRECT) hipLaunchKernelGGL(route_scan, dim3(E + 1), dim3(256), 0, s, nb, E, ws);
-  hipLaunchKernelGGL(route_scatter, dim3(nb), dim3(256), 0, s, ids, R, E, nb, ws, counts, offsets,
+  hipLaunchKernelGGL(route_scatter, dim3(nb), dim3(1024), 0, s, ids, R, E, nb, ws, counts, offsets,
                      sorted_pair, pair_pos, dev_status);
   return launch_status();
 }
