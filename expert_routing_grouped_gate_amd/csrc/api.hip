@@ -525,11 +525,19 @@ int moe_combine(const uint16_t* y, const int32_t* pair_pos, const float* topk_w,
   return moe::launch_combine(y, pair_pos, topk_w, shared_y, T, k, H, out, as_stream(stream));
 }
 
+// Decode front end: the router's partial sums, then (at the next 256-byte
+// boundary) the gate blocks' done counter.
+static bool decode_front(int T, int k) { return T <= 16 && T * k <= 1024; }
+static size_t decode_counter_offset(int T, const MoeLayerDesc* d) {
+  return (moe_router_workspace_size(T, d->H, d->E) + 255) / 256 * 256;
+}
+
 size_t moe_layer_workspace_size(const MoeLayerDesc* d, int T) {
   if (d == nullptr || T <= 0) return 0;
   // the router's partial sums and the routing histograms are live at
   // different times and share the space
-  const size_t r = moe_router_workspace_size(T, d->H, d->E);
+  const size_t r = decode_front(T, d->k) ? decode_counter_offset(T, d) + 256
+                                         : moe_router_workspace_size(T, d->H, d->E);
   const size_t h = moe_route_workspace_size(T, d->k, d->E);
   return r > h ? r : h;
 }
@@ -563,17 +571,20 @@ int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t*
   const int k = d->k;
   const void* xin = mx ? static_cast<const void*>(b->xq) : static_cast<const void*>(x);
   const uint8_t* xin_s = mx ? b->xq_scales : nullptr;
-  if (T <= 16 && T * k <= 1024) {
-    // decode: router partials (+ MXFP8 x), then one block for the rest of the routing
+  if (decode_front(T, k)) {
+    // decode: router partials (+ MXFP8 x), then a block per token for its
+    // top-k, the last one also for the routing
     hipStream_t s = as_stream(stream);
     float* part = static_cast<float*>(b->workspace);
+    int32_t* done = reinterpret_cast<int32_t*>(static_cast<char*>(b->workspace) +
+                                               decode_counter_offset(T, d));
     if ((st = moe::launch_router_partial(x, d->wr, T, d->H, d->E, part, mx ? b->xq : nullptr,
-                                         mx ? b->xq_scales : nullptr, s)))
+                                         mx ? b->xq_scales : nullptr, done, s)))
       return st;
-    if ((st = moe::launch_gate_route_small(part, d->H, d->bias, T, d->E, k, d->gate_mode,
-                                           d->routed_scale, d->eps, b->logits, b->topk_ids,
-                                           b->topk_w, b->counts, b->offsets, b->sorted_pair,
-                                           b->pair_pos, b->dev_status, s)))
+    if ((st = moe::launch_gate_route_decode(part, d->H, d->bias, T, d->E, k, d->gate_mode,
+                                            d->routed_scale, d->eps, b->logits, b->topk_ids,
+                                            b->topk_w, b->counts, b->offsets, b->sorted_pair,
+                                            b->pair_pos, b->dev_status, done, s)))
       return st;
   } else {
     if (mx && (st = moe_mx_quantize(x, T, d->H, b->xq, b->xq_scales, stream))) return st;

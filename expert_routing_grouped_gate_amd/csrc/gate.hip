@@ -53,7 +53,9 @@ __device__ __forceinline__ void split3_bf16(const float* w8, u32x4& hi, u32x4& m
 // xq != nullptr the waves also write the MXFP8
 // quantisation of their x slice (each MX block of 32 is held by the 4 lanes
 // of one token; the expert groups of a slice split its steps), so the W4A8
-// path needs no separate quantiser launch.
+// path needs no separate quantiser launch.  With done != nullptr, block 0
+// zeroes the counter the decode gate's blocks count themselves on (the gate
+// runs after this kernel on the same stream, so it always starts at zero).
 constexpr int RP_HS = 256;
 
 // Many tokens: the MFMA router splits K over ks <= 8 blocks per output tile
@@ -79,10 +81,13 @@ __global__ __launch_bounds__(64) void router_partial(const uint16_t* __restrict_
                                                       const float* __restrict__ wr, int T, int H,
                                                       int E, float* __restrict__ partial,
                                                       uint8_t* __restrict__ xq,
-                                                      uint8_t* __restrict__ xq_scales) {
+                                                      uint8_t* __restrict__ xq_scales,
+                                                      int32_t* __restrict__ done) {
   const int lane = threadIdx.x & 63;
   const int eg = blockIdx.x;
   const int e0 = eg * 16;
+  if (done != nullptr && lane == 0 && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    *done = 0;
   if (e0 >= E) return;  // wave-uniform; the kernel has no barriers
   const int sl = blockIdx.y, h0 = sl * RP_HS, t0 = blockIdx.z * 16;
   const int fr = lane & 15, fc = lane >> 4;
@@ -372,9 +377,10 @@ int launch_router_logits_f32(const float* x, const float* wr, int T, int H, int 
 }
 
 int launch_router_partial(const uint16_t* x, const float* wr, int T, int H, int E,
-                          float* partial, uint8_t* xq, uint8_t* xq_scales, hipStream_t s) {
+                          float* partial, uint8_t* xq, uint8_t* xq_scales, int32_t* done,
+                          hipStream_t s) {
   hipLaunchKernelGGL(router_partial, dim3((E + 15) / 16, H / RP_HS, (T + 15) / 16), dim3(64), 0,
-                     s, x, wr, T, H, E, partial, xq, xq_scales);
+                     s, x, wr, T, H, E, partial, xq, xq_scales, done);
   return launch_status();
 }
 
@@ -384,7 +390,7 @@ int launch_router_partial(const uint16_t* x, const float* wr, int T, int H, int 
 static int launch_router_slices(const uint16_t* x, const float* wr, int T, int H, int E,
                                 float* logits, float* ws, hipStream_t s) {
   if (T <= 64) {
-    launch_router_partial(x, wr, T, H, E, ws, nullptr, nullptr, s);
+    launch_router_partial(x, wr, T, H, E, ws, nullptr, nullptr, nullptr, s);
     return H / RP_HS;
   }
   const int ks = router_ksplit(T, H, E);
@@ -481,13 +487,27 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return (r[0] + r[1]) + (r[2] + r[3]);
 }
 
-// Top-k of one token.  L[i] = logit of expert lane + 64 i (ignored past E).
-// Writes ids[0..k) and weights[0..k) of the token; returns this lane's
-// selected expert for lanes < k.
+// The bias of experts lane + 64 i (0 past E or without a bias).  Loaded
+// before the logits, whose loads it does not depend on, so that the gate
+// waits for one memory round trip, not two.
+template <int NSL>
+__device__ __forceinline__ void load_bias(const float* __restrict__ bias, int E, float (&bv)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    bv[i] = (bias != nullptr && i < NSL && e < E) ? bias[e] : 0.f;
+  }
+}
+
+// Top-k of one token.  L[i] = logit of expert lane + 64 i (ignored past E),
+// bv[i] its bias (load_bias; used only when has_bias).  Writes ids[0..k) and
+// weights[0..k) of the token; returns this lane's selected expert for
+// lanes < k.
 template <int MODE, int NSL>
-__device__ __forceinline__ uint32_t gate_token(const float (&L)[4], const float* __restrict__ bias,
-                                               int E, int k, float routed_scale, float eps,
-                                               int32_t* __restrict__ ids_row,
+__device__ __forceinline__ uint32_t gate_token(const float (&L)[4], const float (&bv)[4],
+                                               bool has_bias, int E, int k, float routed_scale,
+                                               float eps, int32_t* __restrict__ ids_row,
                                                float* __restrict__ w_row) {
   const int lane = threadIdx.x & 63;
   uint32_t khi[NSL], klo[NSL];  // 0 = retired or no expert (below every real key)
@@ -500,11 +520,11 @@ __device__ __forceinline__ uint32_t gate_token(const float (&L)[4], const float*
     sval[i] = 0.0;
     if (e < E) {
       if (MODE == 0) {
-        khi[i] = ord_key32(bias ? (L[i] + bias[e]) : L[i]);  // fp32 add, as the oracle
+        khi[i] = ord_key32(has_bias ? (L[i] + bv[i]) : L[i]);  // fp32 add, as the oracle
       } else {
         const double sg = 1.0 / (1.0 + exp(-(double)L[i]));
         sval[i] = sg;
-        const uint64_t o = ord_key64(bias ? sg + (double)bias[e] : sg);
+        const uint64_t o = ord_key64(has_bias ? sg + (double)bv[i] : sg);
         khi[i] = (uint32_t)(o >> 32);
         klo[i] = (uint32_t)o;
       }
@@ -581,13 +601,15 @@ __global__ __launch_bounds__(256) void gate_topk_kernel(const float* __restrict_
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // wave-uniform; no barriers
+  float bv[4];
+  load_bias<NSL>(bias, E, bv);
   float L[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
     L[i] = e < E ? logits[(size_t)t * E + e] : 0.f;
   }
-  gate_token<MODE, NSL>(L, bias, E, k, routed_scale, eps, ids + (size_t)t * k,
+  gate_token<MODE, NSL>(L, bv, bias != nullptr, E, k, routed_scale, eps, ids + (size_t)t * k,
                         wout + (size_t)t * k);
 }
 
@@ -602,6 +624,8 @@ __global__ __launch_bounds__(256) void gate_topk_slices_kernel(
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // wave-uniform; no barriers
+  float bv[4];
+  load_bias<NSL>(bias, E, bv);
   float L[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -609,47 +633,59 @@ __global__ __launch_bounds__(256) void gate_topk_slices_kernel(
     L[i] = e < E ? sum_slices(partial + (size_t)t * E + e, S, (size_t)T * E) : 0.f;
     if (e < E) logits[(size_t)t * E + e] = L[i];
   }
-  gate_token<MODE, NSL>(L, bias, E, k, routed_scale, eps, ids + (size_t)t * k,
+  gate_token<MODE, NSL>(L, bv, bias != nullptr, E, k, routed_scale, eps, ids + (size_t)t * k,
                         wout + (size_t)t * k);
 }
 
 // --------------------------------------------------- S1+S2+S3/S4, decode ---
-// Few tokens (T <= 16, T*k <= 1024): one block of 1024 threads finishes the
-// routing in one launch after router_partial.  Wave t sums token t's slice
+// Few tokens (T <= 16, T*k <= 1024), after router_partial: one one-wave
+// block per token, each on its own CU.  Block t sums token t's slice
 // partials (slice order, as router_reduce) into its logits, stores them and
-// runs the top-k of gate_token; then the block does init_routing and the
-// expert-token counts ([Qwen3] "GMM enablement and routing optimisation") for
-// the T*k pairs, one pair per thread: within a wave, pairs with the same
-// expert are matched with ballots over the 8 id bits and ranked by lane;
-// across waves through per-wave counts in LDS; expert bases are the exclusive
-// scan of the counts.  The order (expert, then pair index) is the stable
-// counting sort of the standalone route kernels.
+// runs the top-k of gate_token.  Then it counts itself done on a device
+// counter that router_partial zeroed: a release fence, one atomic add; no
+// block waits for another.  The block that counts last (it sees T - 1) takes
+// an acquire fence, so every block's ids are visible to it, and does
+// init_routing and the expert-token counts ([Qwen3] "GMM enablement and
+// routing optimisation") for the T*k pairs: per-expert counts in LDS, their
+// exclusive scan, then the pairs in chunks of 64 in pair order, those with
+// the same expert matched with ballots over the 8 id bits and ranked by lane.
+// The order (expert, then pair index) is the stable counting sort of the
+// standalone route kernels.
 template <int MODE, int NSL>
-__global__ __launch_bounds__(1024) void gate_route_small(
+__global__ __launch_bounds__(64) void gate_route_decode(
     const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E, int k,
     float routed_scale, float eps, float* __restrict__ logits, int32_t* __restrict__ ids,
     float* __restrict__ wout, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos,
-    int32_t* __restrict__ dev_status) {
-  __shared__ int wcnt[16][256];
-  __shared__ int base[256];
-  __shared__ int wsum[4];
-  __shared__ int sids[1024];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (wave < T) {
+    int32_t* __restrict__ dev_status, int32_t* __restrict__ done) {
+  __shared__ int cnt[256];  // per-expert counts, then the next free position
+  __shared__ int last;
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
+  {
+    float bv[4];
+    load_bias<NSL>(bias, E, bv);
     // the partials were written by other CUs (other L2s): issue every load
-    // of this lane (up to 4 experts x 16 slices) before the first add
+    // of this lane (up to 4 experts x 16 slices) before the first add.
+    // Buffer loads: the slice and token go into the scalar offset, the
+    // lane's expert (lanes past E read expert E - 1, ignored) is a fixed
+    // byte offset, so the loads need no per-load address registers
+    const __amdgpu_buffer_rsrc_t pr = mx_rsrc(partial, (uint32_t)(S * T * E) * 4u);
+    int voff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff[i] = min(lane + 64 * i, E - 1) * 4;
     float L[4] = {0.f, 0.f, 0.f, 0.f};
-    const size_t stride = (size_t)T * E;
     for (int s0 = 0; s0 < S; s0 += 16) {
       float q[4][16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
+      for (int u = 0; u < 16; ++u) {
+        // slices past S load slice S - 1 and are not summed: no branches
+        // between the loads
+        const int soff = (min(s0 + u, S - 1) * T + t) * E * 4;
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-          q[i][u] = (e < E && s0 + u < S) ? partial[(size_t)(s0 + u) * stride + (size_t)wave * E + e]
-                                          : 0.f;
+        for (int i = 0; i < 4; ++i)
+          q[i][u] = i < NSL ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pr, voff[i], soff, 0))
+                            : 0.f;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -660,57 +696,77 @@ __global__ __launch_bounds__(1024) void gate_route_small(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
-      if (e < E) logits[(size_t)wave * E + e] = L[i];
+      if (i < NSL && e < E) logits[(size_t)t * E + e] = L[i];
     }
-    const uint32_t my = gate_token<MODE, NSL>(L, bias, E, k, routed_scale, eps,
-                                         ids + (size_t)wave * k, wout + (size_t)wave * k);
-    if (lane < k) sids[wave * k + lane] = (int)my;
+    gate_token<MODE, NSL>(L, bv, bias != nullptr, E, k, routed_scale, eps, ids + (size_t)t * k,
+                          wout + (size_t)t * k);
   }
-  for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+  // this block's stores before its count; the count of the block that sees
+  // T - 1 comes after every other block's
+  __threadfence();
   __syncthreads();
+  if (lane == 0) last = atomicAdd(done, 1) == T - 1;
+  __syncthreads();
+  if (!last) return;  // block-uniform; no barriers after this for the others
+  __threadfence();
   const int R = T * k;
-  const int p = tid;
-  const int e = p < R ? sids[p] : -1;
-  const bool ok = e >= 0 && e < E;
-  unsigned long long match = __ballot(ok);
+  for (int e = lane; e < 256; e += 64) cnt[e] = 0;
+  __syncthreads();
+  bool bad = false;
+  for (int p = lane; p < R; p += 64) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    else bad = true;
+  }
+  __syncthreads();
+  // exclusive scan of the counts: lane l holds experts 4l .. 4l+3 (E <= 256)
+  int v[4], sum = 0;
 #pragma unroll
-  for (int bit = 0; bit < 8; ++bit) {
-    const bool on = ok && ((e >> bit) & 1);
-    const unsigned long long bb = __ballot(on);
-    match &= ((e >> bit) & 1) ? bb : ~bb;
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * lane + j;
+    v[j] = e < E ? cnt[e] : 0;
+    sum += v[j];
   }
-  const int rank = __popcll(match & ((1ull << lane) - 1ull));
-  if (ok && rank == 0) wcnt[wave][e] = __popcll(match);
+  const int incl = wave_incl_scan(sum);
+  int run = incl - sum;
   __syncthreads();
-  // per-expert totals and their exclusive scan (threads 0..255, E <= 256)
-  int v = 0, incl = 0;
-  if (tid < E)
-    for (int w = 0; w < 16; ++w) v += wcnt[w][tid];
-  if (tid < 256) {  // waves 0..3, whole waves
-    incl = wave_incl_scan(v);
-    if (lane == 63) wsum[wave] = incl;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 4 * lane + j;
+    if (e < E) {
+      counts[e] = v[j];
+      offsets[e] = run;
+      cnt[e] = run;
+    }
+    run += v[j];
   }
+  if (lane == 63) offsets[E] = run;
   __syncthreads();
-  if (tid < E) {
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const int excl = before + incl - v;
-    base[tid] = excl;
-    counts[tid] = v;
-    offsets[tid] = excl;
-    if (tid == E - 1) offsets[E] = excl + v;
+  for (int p0 = 0; p0 < R; p0 += 64) {  // chunks in pair order
+    const int p = p0 + lane;
+    const int e = p < R ? ids[p] : -1;
+    const bool ok = e >= 0 && e < E;
+    unsigned long long match = __ballot(ok);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool on = ok && ((e >> bit) & 1);
+      const unsigned long long bb = __ballot(on);
+      match &= ((e >> bit) & 1) ? bb : ~bb;
+    }
+    const int rank = __popcll(match & ((1ull << lane) - 1ull));
+    const int pos = ok ? cnt[e] + rank : -1;
+    __syncthreads();  // every lane has read its expert's position
+    if (ok) {
+      sorted_pair[pos] = p;
+      pair_pos[p] = pos;
+      if (rank == 0) cnt[e] += __popcll(match);
+    } else if (p < R) {
+      pair_pos[p] = -1;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (ok) {
-    int pos = base[e] + rank;
-    for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
-    sorted_pair[pos] = p;
-    pair_pos[p] = pos;
-  } else if (p < R) {
-    pair_pos[p] = -1;
-  }
-  const bool bad = __syncthreads_or(p < R && !ok);
-  if (tid == 0 && dev_status != nullptr) *dev_status = bad ? 1 : 0;
+  const bool any_bad = __ballot(bad) != 0ull;
+  if (lane == 0 && dev_status != nullptr) *dev_status = any_bad ? 1 : 0;
 }
 
 // Slots per lane for E experts (lane l holds experts l + 64 i).
@@ -731,14 +787,14 @@ static void by_mode_slots(int mode, int E, A... args) {
 }
 
 template <int MODE, int NSL>
-struct GateRouteSmall {
+struct GateRouteDecode {
   static void run(hipStream_t s, const float* partial, int S, const float* bias, int T, int E, int k,
                   float routed_scale, float eps, float* logits, int32_t* ids, float* w,
                   int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
-                  int32_t* dev_status) {
-    hipLaunchKernelGGL((gate_route_small<MODE, NSL>), dim3(1), dim3(1024), 0, s, partial, S, bias,
+                  int32_t* dev_status, int32_t* done) {
+    hipLaunchKernelGGL((gate_route_decode<MODE, NSL>), dim3(T), dim3(64), 0, s, partial, S, bias,
                        T, E, k, routed_scale, eps, logits, ids, w, counts, offsets, sorted_pair,
-                       pair_pos, dev_status);
+                       pair_pos, dev_status, done);
   }
 };
 
@@ -773,13 +829,14 @@ int launch_router_gate(const uint16_t* x, const float* wr, int T, int H, int E, 
   return launch_status();
 }
 
-int launch_gate_route_small(const float* partial, int H, const float* bias, int T, int E, int k,
-                            int mode, float routed_scale, float eps, float* logits, int32_t* ids,
-                            float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
-                            int32_t* pair_pos, int32_t* dev_status, hipStream_t s) {
-  by_mode_slots<GateRouteSmall>(mode, E, s, partial, H / RP_HS, bias, T, E, k, routed_scale, eps,
-                                logits, ids, w, counts, offsets, sorted_pair, pair_pos,
-                                dev_status);
+int launch_gate_route_decode(const float* partial, int H, const float* bias, int T, int E, int k,
+                             int mode, float routed_scale, float eps, float* logits, int32_t* ids,
+                             float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                             int32_t* pair_pos, int32_t* dev_status, int32_t* done,
+                             hipStream_t s) {
+  by_mode_slots<GateRouteDecode>(mode, E, s, partial, H / RP_HS, bias, T, E, k, routed_scale, eps,
+                                 logits, ids, w, counts, offsets, sorted_pair, pair_pos,
+                                 dev_status, done);
   return launch_status();
 }
 

@@ -27,15 +27,18 @@ int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E
 size_t router_f32_workspace_bytes(int T, int H, int E);
 int launch_router_logits_f32(const float* x, const float* wr, int T, int H, int E, float* logits,
                              float* ws, hipStream_t s);
-// Few-token layer front end: partial logits (+ MXFP8 x when xq != nullptr),
-// then one block for logits, top-k, counts and the permutation (T <= 16,
-// T*k <= 1024).
+// Few-token layer front end (T <= 16, T*k <= 1024): partial logits (+ MXFP8
+// x when xq != nullptr; done zeroed when not null), then one block per token
+// for its logits and top-k, the last of them also for the counts and the
+// permutation (done: the counter router_partial zeroed).
 int launch_router_partial(const uint16_t* x, const float* wr, int T, int H, int E,
-                          float* partial, uint8_t* xq, uint8_t* xq_scales, hipStream_t s);
-int launch_gate_route_small(const float* partial, int H, const float* bias, int T, int E, int k,
-                            int mode, float routed_scale, float eps, float* logits, int32_t* ids,
-                            float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
-                            int32_t* pair_pos, int32_t* dev_status, hipStream_t s);
+                          float* partial, uint8_t* xq, uint8_t* xq_scales, int32_t* done,
+                          hipStream_t s);
+int launch_gate_route_decode(const float* partial, int H, const float* bias, int T, int E, int k,
+                             int mode, float routed_scale, float eps, float* logits, int32_t* ids,
+                             float* w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                             int32_t* pair_pos, int32_t* dev_status, int32_t* done,
+                             hipStream_t s);
 int launch_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,
                      float routed_scale, float eps, int32_t* ids, float* w, hipStream_t s);
 // S1 + S2 for the layer: the router's slice partials (in ws, of

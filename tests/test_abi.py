@@ -195,8 +195,10 @@ def test_layer_forward_checks(lib):
     assert f(ctypes.byref(d), FAKE, 4, FAKE, ctypes.byref(b), None) == NULL   # buffers unset
     d2 = B.MoeLayerDesc(512, 8, 2, 0, 1.0, 1e-20, FAKE, None, w)
     assert f(ctypes.byref(d2), FAKE, 4, FAKE, ctypes.byref(b), None) == SHAPE  # H mismatch
-    # 16 tokens: the router's partial sums (1 slice x 16 x 8 fp32)
-    assert lib.moe_layer_workspace_size(ctypes.byref(d), 16) == 16 * 8 * 4
+    # 16 tokens: the router's partial sums (1 slice x 16 x 8 fp32), then the
+    # decode gate's done counter at the next 256-byte boundary
+    assert lib.moe_layer_workspace_size(ctypes.byref(d), 16) == 16 * 8 * 4 + 256
+    assert lib.moe_layer_workspace_size(ctypes.byref(d), 3) == 256 + 256   # 3 x 8 fp32, rounded up
     assert lib.moe_layer_workspace_size(ctypes.byref(d), 100) == 8 * 100 * 8 * 4  # split-K router
     for T in (0, 1, 16, 100, 4096):      # the survey's name for the same query
         assert lib.moe_workspace_size(ctypes.byref(d), T) == lib.moe_layer_workspace_size(ctypes.byref(d), T)
