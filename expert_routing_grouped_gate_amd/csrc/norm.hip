@@ -27,8 +27,13 @@ template <int NCH>
 __global__ __launch_bounds__(kNormThreads) void add_rmsnorm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ res,
     const uint16_t* __restrict__ w, int H, float eps, NormOut o) {
-  const size_t off = (size_t)blockIdx.x * H;
-  norm_row<NCH>([&](int, int c) { return ld16(x + off + c); }, res, w, H, eps, blockIdx.x, o);
+  const size_t row = blockIdx.x;
+  const uint16_t* xr = x + row * (size_t)H;
+  u32x4 xv[NCH], rv[NCH], wv[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) xv[j] = ld16(xr + 8 * norm_chunk(j, H / 8));
+  norm_row_loads<NCH>(res, w, H, row, rv, wv);
+  norm_row<NCH>(xv, rv, wv, H, eps, row, o);
 }
 
 template <int NCH>
@@ -42,7 +47,10 @@ __global__ __launch_bounds__(kNormThreads) void combine_add_rmsnorm_kernel(
   const int32_t* pp = pair_pos + (size_t)t * k;
   const float* wt = tw + (size_t)t * k;
   const uint16_t* srow = shared_y ? shared_y + (size_t)t * H : nullptr;
-  // every chunk of this thread combined first (all slot rows in flight at once)
+  // the norm's residual and weight chunks first, then every chunk of this
+  // thread combined (all slot rows in flight at once)
+  u32x4 rv[NCH], wv[NCH];
+  norm_row_loads<NCH>(res, w, H, t, rv, wv);
   u32x4 xv[NCH];
   const int c0 = 8 * (int)threadIdx.x;
   combine_chunks<NCH>(y, pp, wt, srow, k, R, H, c0, xv);
@@ -51,7 +59,7 @@ __global__ __launch_bounds__(kNormThreads) void combine_add_rmsnorm_kernel(
     for (int j = 0; j < NCH; ++j)
       if (c0 + 2048 * j < H) *reinterpret_cast<u32x4*>(out + (size_t)t * H + c0 + 2048 * j) = xv[j];
   }
-  norm_row<NCH>([&](int j, int) { return xv[j]; }, res, w, H, eps, t, o);
+  norm_row<NCH>(xv, rv, wv, H, eps, t, o);
 }
 
 template <int NCH>

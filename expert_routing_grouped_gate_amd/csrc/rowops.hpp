@@ -14,10 +14,10 @@ namespace moe {
 // return zero) ([Qwen3] "GMM enablement and routing optimisation": expert
 // outputs back in token order, summed with the top-k weights; [Hy3] section
 // 1.1: plus the shared expert's row): per element, fp32 accumulation in slot
-// order, the shared row added last, rounded to bf16.  The rows of up to 8
-// slots are loaded for every chunk before any of them is accumulated, so a
-// thread has all its loads in flight at once.  pos >= R (outside the rows of
-// y) or < 0 counts as a dropped pair.
+// order, the shared row added last, rounded to bf16.  The shared row is
+// loaded first and the rows of up to 8 slots are loaded for every chunk
+// before any of them is accumulated, so a thread has all its loads in flight
+// at once.  pos >= R (outside the rows of y) or < 0 counts as a dropped pair.
 template <int NCH>
 __device__ __forceinline__ void combine_chunks(const uint16_t* __restrict__ y,
                                                const int32_t* __restrict__ pp,
@@ -25,10 +25,14 @@ __device__ __forceinline__ void combine_chunks(const uint16_t* __restrict__ y,
                                                const uint16_t* __restrict__ shared_row, int k,
                                                int R, int H, int c0, u32x4 (&res)[NCH]) {
   float acc[NCH][8];
+  u32x4 sv[NCH];
 #pragma unroll
-  for (int j = 0; j < NCH; ++j)
+  for (int j = 0; j < NCH; ++j) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
+    const int c = c0 + 2048 * j;
+    sv[j] = (shared_row != nullptr && c < H) ? ld16(shared_row + c) : u32x4{0u, 0u, 0u, 0u};
+  }
   for (int j0 = 0; j0 < k; j0 += 8) {
     int pos[8];
     u32x4 v[NCH][8];
@@ -61,11 +65,10 @@ __device__ __forceinline__ void combine_chunks(const uint16_t* __restrict__ y,
   for (int j = 0; j < NCH; ++j) {
     const int c = c0 + 2048 * j;
     if (shared_row != nullptr && c < H) {
-      const u32x4 v = ld16(shared_row + c);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[j][2 * q] += bf16_to_f32(v[q] & 0xffffu);
-        acc[j][2 * q + 1] += bf16_to_f32(v[q] >> 16);
+        acc[j][2 * q] += bf16_to_f32(sv[j][q] & 0xffffu);
+        acc[j][2 * q + 1] += bf16_to_f32(sv[j][q] >> 16);
       }
     }
 #pragma unroll
@@ -89,17 +92,46 @@ constexpr int kNormThreads = 256;
 // ([Notes] section 2, "Add and RMSNorm": z = x + r, y_i = z_i /
 // sqrt(mean_j z_j^2 + eps) * w_i).  Thread t holds the 16-byte chunks
 // c = t + 256 j (8 elements each, element offset 8 c = 8 t + 2048 j) in
-// registers: xchunk(j, 8 c) returns the bf16 x of its chunk j; z = x + r in
-// fp32 (exact for bf16 inputs); the sum of squares in fp32 in a fixed order
-// (chunk order per thread, a butterfly over the wave, then the four waves); 1/sqrt(mean + eps) in fp64 once per row;
-// y = z * rstd * w in fp32; the MXFP8 output quantises that y per 32-element
-// block (four consecutive threads) with the rule of moe_mx_quantize.
-// H % 32 == 0; NCH >= ceil(H / 8 / 256).  Contains one block barrier: every
-// thread of the block must call it.
-template <int NCH, class XChunk>
-__device__ __forceinline__ void norm_row(XChunk xchunk, const uint16_t* __restrict__ res,
-                                         const uint16_t* __restrict__ w, int H, float eps,
-                                         size_t row, const NormOut& o) {
+// registers: xv[j] the bf16 x of its chunk j, rv[j] and wv[j] its residual
+// and weight (norm_row_loads); z = x + r in fp32 (exact for bf16 inputs);
+// the sum of squares in fp32 in a fixed order (chunk order per thread, a
+// butterfly over the wave, then the four waves); 1/sqrt(mean + eps) in fp64
+// once per row; y = z * rstd * w in fp32; the MXFP8 output quantises that y
+// per 32-element block (four consecutive threads) with the rule of
+// moe_mx_quantize.  H % 32 == 0; NCH >= ceil(H / 8 / 256).  Contains one
+// block barrier: every thread of the block must call it.
+
+// Chunk j of thread t clamped to the row: chunks past the row load the
+// row's last chunk, which is not used, so that the loads need no branches.
+__device__ __forceinline__ int norm_chunk(int j, int nch) {
+  return min((int)threadIdx.x + kNormThreads * j, nch - 1);
+}
+
+// The residual (zeros without one) and weight chunks of this thread for row
+// `row`.  Issued by the kernels before their other loads' results are used:
+// outputs never overlap inputs, and otherwise the compiler would keep these
+// loads behind the stores of the x chunks.
+template <int NCH>
+__device__ __forceinline__ void norm_row_loads(const uint16_t* __restrict__ res,
+                                               const uint16_t* __restrict__ w, int H, size_t row,
+                                               u32x4 (&rv)[NCH], u32x4 (&wv)[NCH]) {
+  const int nch = H / 8;
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    wv[j] = ld16(w + 8 * norm_chunk(j, nch));
+    rv[j] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (res != nullptr) {
+    const uint16_t* r = res + row * (size_t)H;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) rv[j] = ld16(r + 8 * norm_chunk(j, nch));
+  }
+}
+
+template <int NCH>
+__device__ __forceinline__ void norm_row(const u32x4 (&xv)[NCH], const u32x4 (&rv)[NCH],
+                                         const u32x4 (&wv)[NCH], int H, float eps, size_t row,
+                                         const NormOut& o) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = H / 8;
   const size_t off = row * (size_t)H;
@@ -109,12 +141,10 @@ __device__ __forceinline__ void norm_row(XChunk xchunk, const uint16_t* __restri
   for (int j = 0; j < NCH; ++j) {
     const int c = tid + kNormThreads * j;
     if (c < nch) {
-      const u32x4 xv = xchunk(j, 8 * c);
-      const u32x4 rv = res ? ld16(res + off + 8 * c) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        z[j][2 * i] = bf16_to_f32(xv[i] & 0xffffu) + bf16_to_f32(rv[i] & 0xffffu);
-        z[j][2 * i + 1] = bf16_to_f32(xv[i] >> 16) + bf16_to_f32(rv[i] >> 16);
+        z[j][2 * i] = bf16_to_f32(xv[j][i] & 0xffffu) + bf16_to_f32(rv[j][i] & 0xffffu);
+        z[j][2 * i + 1] = bf16_to_f32(xv[j][i] >> 16) + bf16_to_f32(rv[j][i] >> 16);
       }
       if (o.rout) {
         u32x4 v;
@@ -143,11 +173,10 @@ __device__ __forceinline__ void norm_row(XChunk xchunk, const uint16_t* __restri
     const bool live = c < nch;  // H % 32 == 0: a 32-block's four threads agree
     float y[8];
     if (live) {
-      const u32x4 wv = ld16(w + 8 * c);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        y[2 * i] = z[j][2 * i] * rstd * bf16_to_f32(wv[i] & 0xffffu);
-        y[2 * i + 1] = z[j][2 * i + 1] * rstd * bf16_to_f32(wv[i] >> 16);
+        y[2 * i] = z[j][2 * i] * rstd * bf16_to_f32(wv[j][i] & 0xffffu);
+        y[2 * i + 1] = z[j][2 * i + 1] * rstd * bf16_to_f32(wv[j][i] >> 16);
       }
       if (o.yf) {
         float* p = o.yf + off + 8 * c;
