@@ -487,16 +487,56 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return (r[0] + r[1]) + (r[2] + r[3]);
 }
 
-// The bias of experts lane + 64 i (0 past E or without a bias).  Loaded
-// before the logits, whose loads it does not depend on, so that the gate
-// waits for one memory round trip, not two.
+// The bias of experts lane + 64 i (lanes past E read expert E - 1; 0
+// without a bias).  Loaded before the logits, whose loads it does not depend
+// on, so that the gate waits for one memory round trip, not two.  Buffer
+// loads with no branches: without a bias the descriptor holds no records,
+// and its loads return zeros without a memory access.
 template <int NSL>
 __device__ __forceinline__ void load_bias(const float* __restrict__ bias, int E, float (&bv)[4]) {
   const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t br = mx_rsrc(bias, bias != nullptr ? (uint32_t)E * 4u : 0u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    bv[i] = i < NSL ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                          br, min(lane + 64 * i, E - 1) * 4, 0, 0))
+                    : 0.f;
+}
+
+// Logits of token t (wave-uniform) as the slice-order sum of S partials
+// ([S, T, E] fp32, the summation of router_reduce, so the same bits); lane
+// holds experts lane + 64 i, i < NSL.  The partials were written by other
+// CUs (other L2s), so every load of a batch of 16 slices is issued before
+// the first add.  Buffer loads: slice and token go into the scalar offset,
+// the lane's expert is a fixed byte offset (lanes past E read expert E - 1,
+// ignored), and slices past S load slice S - 1 without being summed, so the
+// loads need no address registers and no branches.  S * T * E * 4 < 2^31.
+template <int NSL>
+__device__ __forceinline__ void sum_token_slices(const float* __restrict__ partial, int S, int T,
+                                                 int E, int t, float (&L)[4]) {
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t pr = mx_rsrc(partial, (uint32_t)S * (uint32_t)T * (uint32_t)E * 4u);
+  int voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    bv[i] = (bias != nullptr && i < NSL && e < E) ? bias[e] : 0.f;
+    voff[i] = min(lane + 64 * i, E - 1) * 4;
+    L[i] = 0.f;
+  }
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    float q[4][16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int soff = __builtin_amdgcn_readfirstlane((min(s0 + u, S - 1) * T + t) * E * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        q[i][u] = i < NSL ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pr, voff[i], soff, 0))
+                          : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (s0 + u < S) L[i] = (s0 + u == 0) ? q[i][u] : L[i] + q[i][u];
   }
 }
 
@@ -627,11 +667,11 @@ __global__ __launch_bounds__(256) void gate_topk_slices_kernel(
   float bv[4];
   load_bias<NSL>(bias, E, bv);
   float L[4];
+  sum_token_slices<NSL>(partial, S, T, E, t, L);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    L[i] = e < E ? sum_slices(partial + (size_t)t * E + e, S, (size_t)T * E) : 0.f;
-    if (e < E) logits[(size_t)t * E + e] = L[i];
+    if (i < NSL && e < E) logits[(size_t)t * E + e] = L[i];
   }
   gate_token<MODE, NSL>(L, bv, bias != nullptr, E, k, routed_scale, eps, ids + (size_t)t * k,
                         wout + (size_t)t * k);
@@ -665,34 +705,8 @@ __global__ __launch_bounds__(64) void gate_route_decode(
   {
     float bv[4];
     load_bias<NSL>(bias, E, bv);
-    // the partials were written by other CUs (other L2s): issue every load
-    // of this lane (up to 4 experts x 16 slices) before the first add.
-    // Buffer loads: the slice and token go into the scalar offset, the
-    // lane's expert (lanes past E read expert E - 1, ignored) is a fixed
-    // byte offset, so the loads need no per-load address registers
-    const __amdgpu_buffer_rsrc_t pr = mx_rsrc(partial, (uint32_t)(S * T * E) * 4u);
-    int voff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) voff[i] = min(lane + 64 * i, E - 1) * 4;
-    float L[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S; s0 += 16) {
-      float q[4][16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        // slices past S load slice S - 1 and are not summed: no branches
-        // between the loads
-        const int soff = (min(s0 + u, S - 1) * T + t) * E * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          q[i][u] = i < NSL ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pr, voff[i], soff, 0))
-                            : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (s0 + u < S) L[i] = (s0 + u == 0) ? q[i][u] : L[i] + q[i][u];
-    }
+    float L[4];
+    sum_token_slices<NSL>(partial, S, T, E, t, L);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
