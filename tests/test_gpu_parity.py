@@ -280,12 +280,37 @@ def test_layer_small(name):
     _layer_check(SMALL[name])
 
 
+@pytest.mark.parametrize("name", ["tiny", "small_hy3_decode", "wide_k_decode"])
+def test_decode_routing_on_repeated_calls(name):
+    """With T <= 16 the routing is done by whichever token block finishes
+    last, found through a done counter that the router launch zeroes on
+    every call.  Calls in a row on one layer (one workspace), with other
+    tokens each time, must each give what a fresh layer gives: a counter
+    left at a stale value would skip the routing and keep the previous
+    call's permutation."""
+    cfg = SMALL[name]
+    L = get_layer(cfg)
+    x1 = L.dev["x"]
+    x2 = torch.flip(x1, dims=[0]).contiguous()    # other tokens in every row
+    layer = L.layer()
+    for i, x in enumerate((x1, x2, x1, x2)):
+        out = layer.forward(x).clone()
+        fresh = L.layer()
+        fout = fresh.forward(x)
+        torch.cuda.synchronize()
+        assert torch.equal(out, fout), f"call {i}: output"
+        for key in ("logits", "topk_ids", "topk_w", "counts", "offsets", "sorted_pair", "pair_pos"):
+            assert torch.equal(layer.buf[key], fresh.buf[key]), f"call {i}: {key}"
+    log(f"[{cfg.name}] four calls in a row routed as fresh layers")
+
+
 @pytest.mark.parametrize("name", ["tiny", "small_hy3_decode", "wide_k_decode", "wide_k", "small_hy3",
                                   "small_prefill", "tiled4_stream"])
 def test_layer_routing_equals_the_step_calls(name):
     """The layer's own routing launches must equal the standalone router,
     gate and route calls bit for bit: with T <= 16 the router partial sums,
-    then one block for logits, top-k, counts and permutation; with more
+    then a block per token for logits and top-k, the last of them to finish
+    also for counts and permutation; with more
     tokens the router's slice partials summed inside the gate (one slice at
     H = 256 and T <= 64, eight K-split tiles of one- or two-step stages
     above)."""
