@@ -349,8 +349,10 @@ typedef struct {
   uint8_t* shared_act_scales;
   uint16_t* shared_y;     /* [T, H] */
   void* workspace;        /* moe_layer_workspace_size(desc, T) bytes (router
-                             partial sums or routing histograms; one call at
-                             a time per workspace) */
+                             partial sums or routing histograms; with at most
+                             16 tokens also the gate blocks' done counter,
+                             which the call zeroes itself; one call at a time
+                             per workspace) */
   size_t workspace_bytes;
   /* Optional hipEvent_t handles, recorded on `stream` right before and right
    * after the grouped GEMM1 (w13 + SwiGLU) launch so that a caller can time
