@@ -587,11 +587,12 @@ int moe_layer_forward(const MoeLayerDesc* d, const uint16_t* x, int T, uint16_t*
                                             b->pair_pos, b->dev_status, done, s)))
       return st;
   } else {
-    if (mx && (st = moe_mx_quantize(x, T, d->H, b->xq, b->xq_scales, stream))) return st;
-    // router and gate (the router's slice partials are summed inside the gate)
+    // router (+ the MXFP8 codes of x for W4A8) and gate (the router's slice
+    // partials are summed inside the gate)
     if ((st = moe::launch_router_gate(x, d->wr, T, d->H, d->E, k, d->gate_mode, d->routed_scale,
                                       d->eps, d->bias, b->logits, b->topk_ids, b->topk_w,
-                                      static_cast<float*>(b->workspace), as_stream(stream))))
+                                      static_cast<float*>(b->workspace), mx ? b->xq : nullptr,
+                                      mx ? b->xq_scales : nullptr, as_stream(stream))))
       return st;
     if ((st = moe_route(b->topk_ids, T, k, d->E, b->counts, b->offsets, b->sorted_pair,
                         b->pair_pos, b->dev_status, b->workspace, b->workspace_bytes, stream)))

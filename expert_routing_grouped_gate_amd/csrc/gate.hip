@@ -185,13 +185,20 @@ __global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ p
 // (four 16-expert groups x three parts: 24 MFMAs per K step).  Each
 // accumulator takes its K-steps in order, the three parts of a step in the
 // order hi, mid, lo, whatever KS is.  Block z of gridDim.z covers the z-th
-// 1/gridDim.z of K and writes its partial tile to logits + z*T*E.
+// 1/gridDim.z of K and writes its partial tile to logits + z*T*E.  With
+// xq != nullptr (W4A8 layers) the blocks of the first expert tile also write
+// the MXFP8 codes of the x slice they load, so that every element is
+// quantised once over the K split and no separate quantiser reads x again: a
+// 32-column block of one row is the four loading threads of that row, and
+// the arithmetic is mx_quant_kernel's.
 
 template <int KS>
 __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ wr, int T,
                                                           int H, int E,
-                                                          float* __restrict__ logits) {
+                                                          float* __restrict__ logits,
+                                                          uint8_t* __restrict__ xq,
+                                                          uint8_t* __restrict__ xq_scales) {
   __shared__ u32x4 xs[2][KS][RM_TT * 4];
   __shared__ u32x4 ws[2][KS][3][RM_TE * 4];
   const int tid = threadIdx.x;
@@ -225,7 +232,39 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
       r.w[j][4] = b.x; r.w[j][5] = b.y; r.w[j][6] = b.z; r.w[j][7] = b.w;
     }
   };
-  auto lstore = [&](const Regs& r, int buf) {
+  const bool quant = xq != nullptr && blockIdx.y == 0;  // block-uniform
+  // 8 consecutive elements of x row `row` at column `col`: the four threads
+  // of the row's 32-column block share one scale
+  auto quant8 = [&](const u32x4 v, int row, int col) {
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = bf16_to_f32(v[q] & 0xffffu);
+      f[2 * q + 1] = bf16_to_f32(v[q] >> 16);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int e = mx_exponent(amax);
+    const float inv = exp2_neg(e);
+    const uint32_t lo = e4m3_pack4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+    const uint32_t hi = e4m3_pack4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+    if (row < T) {
+      *reinterpret_cast<u32x2*>(xq + (size_t)row * H + col) = u32x2{lo, hi};
+      if (lch == 0) xq_scales[(size_t)row * (H / 32) + col / 32] = (uint8_t)(e + 127);
+    }
+  };
+  auto lstore = [&](const Regs& r, int buf, int k0) {
+    if (quant) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const int col = kbeg + k0 + 32 * j + lch * 8;
+        quant8(r.xa[j], t0 + lrow, col);
+        quant8(r.xb[j], t0 + 64 + lrow, col);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
       xs[buf][j][lrow * 4 + lch] = r.xa[j];
@@ -261,17 +300,17 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
   constexpr int KW = 32 * KS;  // columns per stage
   gload(r0, 0);
   if (nk > 1) gload(r1, KW);
-  lstore(r0, 0);
+  lstore(r0, 0, 0);
   __syncthreads();
   for (int kt = 0; kt < nk; kt += 2) {
     if (kt + 2 < nk) gload(r0, (kt + 2) * KW);
     compute(0);
-    if (kt + 1 < nk) lstore(r1, 1);
+    if (kt + 1 < nk) lstore(r1, 1, (kt + 1) * KW);
     __syncthreads();
     if (kt + 1 >= nk) break;
     if (kt + 3 < nk) gload(r1, (kt + 3) * KW);
     compute(1);
-    if (kt + 2 < nk) lstore(r0, 0);
+    if (kt + 2 < nk) lstore(r0, 0, (kt + 2) * KW);
     __syncthreads();
   }
   // D[m][n]: lane holds expert 16*g + (lane & 15), tokens 16*mi + 4*(lane>>4) + i
@@ -386,11 +425,13 @@ int launch_router_partial(const uint16_t* x, const float* wr, int T, int H, int 
 
 // The partial-sum kernels of S1: returns the number S of slice partials
 // written to ws ([S, T, E], summed in slice order afterwards), or 0 when the
-// logits were written directly.
+// logits were written directly.  With xq != nullptr they also write the
+// MXFP8 codes and scales of x.
 static int launch_router_slices(const uint16_t* x, const float* wr, int T, int H, int E,
-                                float* logits, float* ws, hipStream_t s) {
+                                float* logits, float* ws, uint8_t* xq, uint8_t* xq_scales,
+                                hipStream_t s) {
   if (T <= 64) {
-    launch_router_partial(x, wr, T, H, E, ws, nullptr, nullptr, nullptr, s);
+    launch_router_partial(x, wr, T, H, E, ws, xq, xq_scales, nullptr, s);
     return H / RP_HS;
   }
   const int ks = router_ksplit(T, H, E);
@@ -399,15 +440,17 @@ static int launch_router_slices(const uint16_t* x, const float* wr, int T, int H
   // two 32-column steps per stage when every block's K range holds an even
   // number of them (the same sums either way)
   if ((H / 32 / ks) % 2 == 0)
-    hipLaunchKernelGGL(router_logits_mfma<2>, grid, dim3(256), 0, s, x, wr, T, H, E, dst);
+    hipLaunchKernelGGL(router_logits_mfma<2>, grid, dim3(256), 0, s, x, wr, T, H, E, dst, xq,
+                       xq_scales);
   else
-    hipLaunchKernelGGL(router_logits_mfma<1>, grid, dim3(256), 0, s, x, wr, T, H, E, dst);
+    hipLaunchKernelGGL(router_logits_mfma<1>, grid, dim3(256), 0, s, x, wr, T, H, E, dst, xq,
+                       xq_scales);
   return ks > 1 ? ks : 0;
 }
 
 int launch_router_logits(const uint16_t* x, const float* wr, int T, int H, int E, float* logits,
                          float* ws, hipStream_t s) {
-  const int S = launch_router_slices(x, wr, T, H, E, logits, ws, s);
+  const int S = launch_router_slices(x, wr, T, H, E, logits, ws, nullptr, nullptr, s);
   if (S > 0)
     hipLaunchKernelGGL(router_reduce, dim3((T * E + 255) / 256), dim3(256), 0, s, ws, S, T, E,
                        logits);
@@ -832,8 +875,9 @@ struct GateTopkSlices {
 
 int launch_router_gate(const uint16_t* x, const float* wr, int T, int H, int E, int k, int mode,
                        float routed_scale, float eps, const float* bias, float* logits,
-                       int32_t* ids, float* w, float* ws, hipStream_t s) {
-  const int S = launch_router_slices(x, wr, T, H, E, logits, ws, s);
+                       int32_t* ids, float* w, float* ws, uint8_t* xq, uint8_t* xq_scales,
+                       hipStream_t s) {
+  const int S = launch_router_slices(x, wr, T, H, E, logits, ws, xq, xq_scales, s);
   if (S > 0)
     by_mode_slots<GateTopkSlices>(mode, E, s, static_cast<const float*>(ws), S, bias, T, E, k,
                                   routed_scale, eps, logits, ids, w);

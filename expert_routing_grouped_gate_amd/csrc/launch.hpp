@@ -42,10 +42,13 @@ int launch_gate_route_decode(const float* partial, int H, const float* bias, int
 int launch_gate_topk(const float* logits, const float* bias, int T, int E, int k, int mode,
                      float routed_scale, float eps, int32_t* ids, float* w, hipStream_t s);
 // S1 + S2 for the layer: the router's slice partials (in ws, of
-// router_workspace_bytes) summed inside the gate, logits stored on the way.
+// router_workspace_bytes) summed inside the gate, logits stored on the way;
+// with xq != nullptr the router kernels also write x's MXFP8 codes and
+// scales (S0 of the W4A8 layer).
 int launch_router_gate(const uint16_t* x, const float* wr, int T, int H, int E, int k, int mode,
                        float routed_scale, float eps, const float* bias, float* logits,
-                       int32_t* ids, float* w, float* ws, hipStream_t s);
+                       int32_t* ids, float* w, float* ws, uint8_t* xq, uint8_t* xq_scales,
+                       hipStream_t s);
 
 size_t route_workspace_bytes(int T, int k, int E);
 int launch_route(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
