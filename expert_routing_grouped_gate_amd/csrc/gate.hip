@@ -186,11 +186,13 @@ __global__ __launch_bounds__(256) void router_reduce(const float* __restrict__ p
 // accumulator takes its K-steps in order, the three parts of a step in the
 // order hi, mid, lo, whatever KS is.  Block z of gridDim.z covers the z-th
 // 1/gridDim.z of K and writes its partial tile to logits + z*T*E.  With
-// xq != nullptr (W4A8 layers) the blocks of the first expert tile also write
-// the MXFP8 codes of the x slice they load, so that every element is
-// quantised once over the K split and no separate quantiser reads x again: a
-// 32-column block of one row is the four loading threads of that row, and
-// the arithmetic is mx_quant_kernel's.
+// xq != nullptr (W4A8 layers) blocks also write the MXFP8 codes of the x
+// slice they load, so that no separate quantiser reads x again: the first
+// expert tile's blocks the tile's first 64 rows, the second's the other 64
+// (the first's all 128 when there is one expert tile), so that every
+// element is quantised once over the K split.  A 32-column block of one row
+// is the four loading threads of that row; the arithmetic is
+// mx_quant_kernel's.
 
 template <int KS>
 __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x,
@@ -232,7 +234,9 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
       r.w[j][4] = b.x; r.w[j][5] = b.y; r.w[j][6] = b.z; r.w[j][7] = b.w;
     }
   };
-  const bool quant = xq != nullptr && blockIdx.y == 0;  // block-uniform
+  // block-uniform: which of the tile's row halves this block quantises
+  const bool quant_a = xq != nullptr && blockIdx.y == 0;
+  const bool quant_b = xq != nullptr && blockIdx.y == (gridDim.y > 1 ? 1u : 0u);
   // 8 consecutive elements of x row `row` at column `col`: the four threads
   // of the row's 32-column block share one scale
   auto quant8 = [&](const u32x4 v, int row, int col) {
@@ -257,13 +261,11 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
     }
   };
   auto lstore = [&](const Regs& r, int buf, int k0) {
-    if (quant) {
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        const int col = kbeg + k0 + 32 * j + lch * 8;
-        quant8(r.xa[j], t0 + lrow, col);
-        quant8(r.xb[j], t0 + 64 + lrow, col);
-      }
+    for (int j = 0; j < KS; ++j) {
+      const int col = kbeg + k0 + 32 * j + lch * 8;
+      if (quant_a) quant8(r.xa[j], t0 + lrow, col);
+      if (quant_b) quant8(r.xb[j], t0 + 64 + lrow, col);
     }
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
