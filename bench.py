@@ -118,8 +118,9 @@ class TimingEvent:
             hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
             hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             TimingEvent._hip = hip
+        self._lib = TimingEvent._hip   # (held by the instance: module globals may be gone in __del__)
         h = ctypes.c_void_p()
-        rc = TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE)
+        rc = self._lib.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE)
         if rc != 0:
             raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
         self.cuda_event = h.value   # the handle MoeLayer.time_ffn_up passes to the library
@@ -140,8 +141,12 @@ class TimingEvent:
         return float(f.value)
 
     def __del__(self):
-        if TimingEvent._hip is not None and getattr(self, "cuda_event", None):
-            TimingEvent._hip.hipEventDestroy(self.cuda_event)
+        lib, ev = getattr(self, "_lib", None), getattr(self, "cuda_event", None)
+        if lib is not None and ev:
+            try:
+                lib.hipEventDestroy(ev)
+            except Exception:   # interpreter shutdown: nothing left to release to
+                pass
 
 
 def graded_kernel(config: str):
