@@ -128,14 +128,14 @@ class TimingEvent:
     def record(self, stream_handle) -> None:
         """Record on a stream (a hipStream_t handle, e.g. torch's
         current_stream().cuda_stream)."""
-        rc = TimingEvent._hip.hipEventRecord(self.cuda_event, stream_handle)
+        rc = self._lib.hipEventRecord(self.cuda_event, stream_handle)
         if rc != 0:
             raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, end: "TimingEvent") -> float:
         import ctypes
         f = ctypes.c_float()
-        rc = TimingEvent._hip.hipEventElapsedTime(ctypes.byref(f), self.cuda_event, end.cuda_event)
+        rc = self._lib.hipEventElapsedTime(ctypes.byref(f), self.cuda_event, end.cuda_event)
         if rc != 0:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return float(f.value)
