@@ -98,6 +98,11 @@ for _T in (64, 128, 256, 512, 1024):
     CONFIGS[f"qwen3_w4a8_T{_T}"] = CONFIGS["qwen3_decode_w4a8"].with_(name=f"qwen3_w4a8_T{_T}", T=_T,
                                                                       x_seed=200 + _T)
 
+# The Hy3-style layer at decode size (same weights): the few-token front end
+# with sigmoid gating over 192 experts, and the shared expert on its own
+# weight-streaming launches.
+CONFIGS["hy3_decode"] = CONFIGS["hy3"].with_(name="hy3_decode", T=16, x_seed=300)
+
 
 def _seed(*parts: int) -> int:
     ss = np.random.SeedSequence([int(p) & 0xFFFFFFFF for p in parts])

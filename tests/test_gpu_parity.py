@@ -398,7 +398,7 @@ def test_layer_graph_capture_replays(name):
 # full-size layers: GPU computes everything; routing is checked on all
 # tokens, values on a sample of tokens the oracle evaluates one by one
 FULL = [("qwen3_decode", None), ("qwen3_prefill", [0, 1, 2, 777, 2048, 4094, 4095]),
-        ("hy3", [0, 5, 1023, 1024, 3000, 4095])]
+        ("hy3", [0, 5, 1023, 1024, 3000, 4095]), ("hy3_decode", None)]
 
 
 @pytest.mark.parametrize("name,tokens", FULL, ids=[f[0] for f in FULL])

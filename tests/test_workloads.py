@@ -68,3 +68,10 @@ def test_mid_size_configs_share_the_decode_weights():
         d = W.CONFIGS["qwen3_decode_w4a8"]
         assert c.T == T and (c.family_seed, c.fmt, c.bias) == (d.family_seed, d.fmt, d.bias)
         assert (c.H, c.E, c.k, c.I) == (4096, 128, 8, 1536)
+
+
+def test_hy3_decode_shares_the_hy3_weights():
+    c, h = W.CONFIGS["hy3_decode"], W.CONFIGS["hy3"]
+    assert c.T == 16 and c.x_seed != h.x_seed
+    assert (c.H, c.E, c.k, c.I, c.shared_I, c.gate, c.bias, c.family_seed) == \
+        (h.H, h.E, h.k, h.I, h.shared_I, h.gate, h.bias, h.family_seed)
