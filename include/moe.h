@@ -314,12 +314,13 @@ int moe_combine(const uint16_t* y, const int32_t* pair_pos, const float* topk_w,
                 void* stream);
 
 /* ------------------------------------------------------ whole layer -----
- * S0..S7 in one call on one stream.  With T <= 16 and T*k <= 1024 (decode)
- * the front end is two launches: router partial sums (which also write the
- * MXFP8 x of the W4A8 path) and one block for logits, top-k, counts and the
- * permutation; the shared expert runs inside the routed GEMM launches as
- * moe_grouped_ffn describes; the buffers receive the same values as the
- * per-step calls. */
+ * S0..S7 in one call on one stream.  The router launch also writes the
+ * MXFP8 x of the W4A8 path (no separate quantiser).  With T <= 16 and
+ * T*k <= 1024 (decode) the front end is two launches: router partial sums,
+ * then one block per token for its logits and top-k, the last of them to
+ * finish also for the counts and the permutation; the shared expert runs
+ * inside the routed GEMM launches as moe_grouped_ffn describes; the buffers
+ * receive the same values as the per-step calls. */
 typedef struct {
   int H, E, k;
   int gate_mode;        /* moe_gate_mode */
